@@ -1,0 +1,285 @@
+"""Seeded synthetic workloads for the DFlash2 draft-and-verify step.
+
+This module only draws inputs. It holds none of the step's arithmetic, and both the GPU
+library's tests and the CPU oracle consume exactly the arrays it returns (bf16 values are
+rounded once, here, and passed around as their 16-bit patterns).
+
+Shapes follow the drafter geometry of the pages (block of 8 = anchor + 7 masks, 32 query
+heads, 8 KV heads, head dim 128, 2048-position window, width 5120 with groups of 16, vocab
+248320, top-16, rank-256 codebooks, 5 drafter layers with 4 conv sites each). Variances are
+read as variances: N(0, 4) has standard deviation 2; the heavy-tailed codebooks are
+0.25 * Student-t(3).
+
+Every tensor has its own numpy stream keyed by (config seed, tensor id, layer or site,
+sequence, input set), so any sequence can be regenerated on its own, and one sequence's
+values do not depend on the batch size.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+# ------------------------------------------------------------------------------------------
+# bf16 helpers (input construction only: one round-to-nearest-even narrowing)
+# ------------------------------------------------------------------------------------------
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round binary32 values to bf16 (nearest, ties to even) and return the 16-bit patterns."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounding = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    out = ((u + rounding) >> np.uint32(16)).astype(np.uint16)
+    nan = np.isnan(np.asarray(x, dtype=np.float32))
+    if nan.any():
+        out[nan] = np.uint16(0x7FC0)
+    return out
+
+
+def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
+    return (np.asarray(h, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+# ------------------------------------------------------------------------------------------
+# Configurations
+# ------------------------------------------------------------------------------------------
+
+
+@dataclass(frozen=True)
+class Config:
+    cfg: int
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    S: int
+    W: int
+    C: int
+    V: int
+    R: int
+    layers: int
+    act_bf16: bool            # q/k/v and conv activations in bf16 (else f32)
+    draft_var: float
+    target_noise_var: float
+    target_kind: str          # "logits" (greedy only, same dtype as draft) or "probs" (f32)
+    temperature: tuple        # per-sequence rule: ("all", T) or ("alternate", T_even, T_odd)
+    ctx: tuple                # ("fixed", L) or ("uniform", lo, hi)
+    quantize_draft: float = 0.0  # draft logits rounded to multiples of this (0 = off)
+    heavy_codebooks: bool = False
+    P: int = 8
+    group: int = 16
+    conv_sites_per_layer: int = 4
+
+    @property
+    def N(self) -> int:
+        return self.P - 1
+
+    @property
+    def G(self) -> int:
+        return self.C // self.group
+
+    @property
+    def sites(self) -> int:
+        return self.layers * self.conv_sites_per_layer
+
+    @property
+    def seed(self) -> int:
+        """Philox seed of the step's random draws."""
+        return 0xDF20000 + self.cfg
+
+    def temperatures(self) -> np.ndarray:
+        rule = self.temperature
+        if rule[0] == "all":
+            return np.full(self.B, rule[1], dtype=np.float32)
+        t = np.empty(self.B, dtype=np.float32)
+        t[0::2] = rule[1]
+        t[1::2] = rule[2]
+        return t
+
+
+CONFIGS = {
+    1: Config(1, "tiny-fp32-smoke", B=1, Hq=4, Hkv=1, D=64, S=128, W=64, C=256, V=1024, R=16,
+              layers=1, act_bf16=False, draft_var=3.0, target_noise_var=1.0,
+              target_kind="logits", temperature=("all", 0.0), ctx=("fixed", 128)),
+    2: Config(2, "qwen3.8-27b-drafter-b1-greedy", B=1, Hq=32, Hkv=8, D=128, S=2048, W=2048,
+              C=5120, V=248320, R=256, layers=5, act_bf16=True, draft_var=4.0,
+              target_noise_var=1.5, target_kind="logits", temperature=("all", 0.0),
+              ctx=("fixed", 3000)),
+    3: Config(3, "b16-sampled-t0.7", B=16, Hq=32, Hkv=8, D=128, S=2048, W=2048, C=5120,
+              V=248320, R=256, layers=5, act_bf16=True, draft_var=4.0, target_noise_var=1.5,
+              target_kind="probs", temperature=("all", 0.7), ctx=("uniform", 512, 8192)),
+    4: Config(4, "b16-low-acceptance", B=16, Hq=32, Hkv=8, D=128, S=2048, W=2048, C=5120,
+              V=248320, R=256, layers=5, act_bf16=True, draft_var=4.0, target_noise_var=4.0,
+              target_kind="probs", temperature=("all", 0.7), ctx=("uniform", 512, 8192),
+              quantize_draft=0.25, heavy_codebooks=True),
+    5: Config(5, "b64-serving-mixed", B=64, Hq=32, Hkv=8, D=128, S=2048, W=2048, C=5120,
+              V=248320, R=256, layers=5, act_bf16=True, draft_var=4.0, target_noise_var=1.5,
+              target_kind="probs", temperature=("alternate", 0.0, 1.0),
+              ctx=("uniform", 2048, 131072)),
+}
+
+# tensor ids of the per-tensor streams
+_T_CTX, _T_Q, _T_KBLK, _T_VBLK, _T_KRING, _T_VRING = 1, 2, 3, 4, 5, 6
+_T_X, _T_BASE, _T_DELTA = 7, 8, 9
+_T_DRAFT, _T_TNOISE, _T_PRED, _T_SUCC, _T_GATE, _T_ANCHOR = 10, 11, 12, 13, 14, 15
+
+
+def _rng(cfg: Config, tensor: int, *more: int) -> np.random.Generator:
+    return np.random.default_rng([1000 + cfg.cfg, tensor, *more])
+
+
+def _normal(rng, shape, var=1.0) -> np.ndarray:
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if var != 1.0:
+        x *= np.float32(np.sqrt(var))
+    return x
+
+
+def _act(cfg: Config, x: np.ndarray) -> np.ndarray:
+    return to_bf16_bits(x) if cfg.act_bf16 else x.astype(np.float32)
+
+
+# ------------------------------------------------------------------------------------------
+# Per-tensor generators. `seqs` selects sequences (default all); `iset` picks an input set
+# (the benchmark rotates several so that its working set does not sit in the last-level
+# cache).
+# ------------------------------------------------------------------------------------------
+
+
+def ctx_len(cfg: Config, iset: int = 0) -> np.ndarray:
+    if cfg.ctx[0] == "fixed":
+        return np.full(cfg.B, cfg.ctx[1], dtype=np.int32)
+    lo, hi = cfg.ctx[1], cfg.ctx[2]
+    return _rng(cfg, _T_CTX, iset).integers(lo, hi + 1, size=cfg.B, dtype=np.int64).astype(np.int32)
+
+
+def _per_seq(cfg, tensor, layer, seqs, iset, shape, gen):
+    seqs = range(cfg.B) if seqs is None else seqs
+    return np.stack([gen(_rng(cfg, tensor, layer, b, iset), shape) for b in seqs])
+
+
+def attn_q(cfg: Config, layer: int, seqs=None, iset: int = 0) -> np.ndarray:
+    return _act(cfg, _per_seq(cfg, _T_Q, layer, seqs, iset, (cfg.P, cfg.Hq, cfg.D), _normal))
+
+
+def attn_block_kv(cfg: Config, layer: int, seqs=None, iset: int = 0):
+    shp = (cfg.P, cfg.Hkv, cfg.D)
+    return (_act(cfg, _per_seq(cfg, _T_KBLK, layer, seqs, iset, shp, _normal)),
+            _act(cfg, _per_seq(cfg, _T_VBLK, layer, seqs, iset, shp, _normal)))
+
+
+def attn_ring(cfg: Config, layer: int, seqs=None, iset: int = 0):
+    shp = (cfg.S, cfg.Hkv, cfg.D)
+    return (_act(cfg, _per_seq(cfg, _T_KRING, layer, seqs, iset, shp, _normal)),
+            _act(cfg, _per_seq(cfg, _T_VRING, layer, seqs, iset, shp, _normal)))
+
+
+def conv_inputs(cfg: Config, site: int, seqs=None, iset: int = 0):
+    """x [B,P,C] ~ N(0,1); base [2,C] ~ U(-1,1) (one per site); delta [B,P,2,G] ~ U(-1,1)."""
+    x = _act(cfg, _per_seq(cfg, _T_X, site, seqs, iset, (cfg.P, cfg.C), _normal))
+    base = _rng(cfg, _T_BASE, site).uniform(-1, 1, size=(2, cfg.C)).astype(np.float32)
+    delta = _per_seq(cfg, _T_DELTA, site, seqs, iset, (cfg.P, 2, cfg.G),
+                     lambda r, s: r.uniform(-1, 1, size=s).astype(np.float32))
+    return x, base, delta
+
+
+def draft_logits(cfg: Config, seqs=None, iset: int = 0) -> np.ndarray:
+    """[B, P, V] draft logits: f32 for the tiny config, bf16 bits otherwise."""
+    def gen(r, s):
+        x = _normal(r, s, cfg.draft_var)
+        if cfg.quantize_draft:
+            x = (np.round(x / cfg.quantize_draft) * cfg.quantize_draft).astype(np.float32)
+        return x
+    x = _per_seq(cfg, _T_DRAFT, 0, seqs, iset, (cfg.P, cfg.V), gen)
+    return _act(cfg, x)
+
+
+def target_rows(cfg: Config, draft: np.ndarray, seqs=None, iset: int = 0) -> np.ndarray:
+    """Target rows [B, P, V]: draft + noise as logits (same dtype as the draft), or as f32
+    probabilities softmax(logits / T) (T = 1 for greedy sequences)."""
+    seqs_l = list(range(cfg.B)) if seqs is None else list(seqs)
+    d = bf16_bits_to_f32(draft) if draft.dtype == np.uint16 else draft
+    noise = _per_seq(cfg, _T_TNOISE, 0, seqs_l, iset, (cfg.P, cfg.V),
+                     lambda r, s: _normal(r, s, cfg.target_noise_var))
+    logits = d.astype(np.float32) + noise
+    if cfg.target_kind == "logits":
+        return _act(cfg, logits)
+    temps = cfg.temperatures()[seqs_l]
+    out = np.empty(logits.shape, dtype=np.float32)
+    for n, T in enumerate(temps):
+        z = logits[n].astype(np.float64) / (float(T) if T > 0 else 1.0)
+        z -= z.max(axis=-1, keepdims=True)
+        e = np.exp(z)
+        out[n] = (e / e.sum(axis=-1, keepdims=True)).astype(np.float32)
+    return out
+
+
+def codebooks(cfg: Config):
+    """Predecessor and successor codebooks [V, R] as bf16 bits."""
+    out = []
+    for t in (_T_PRED, _T_SUCC):
+        r = _rng(cfg, t)
+        if cfg.heavy_codebooks:
+            x = (0.25 * r.standard_t(3, size=(cfg.V, cfg.R))).astype(np.float32)
+        else:
+            x = _normal(r, (cfg.V, cfg.R), 1.0 / 16.0)
+        out.append(to_bf16_bits(x))
+    return out[0], out[1]
+
+
+def gate(cfg: Config, seqs=None, iset: int = 0) -> np.ndarray:
+    return _per_seq(cfg, _T_GATE, 0, seqs, iset, (cfg.N, cfg.R), _normal)
+
+
+def anchor(cfg: Config, iset: int = 0) -> np.ndarray:
+    return _rng(cfg, _T_ANCHOR, iset).integers(0, cfg.V, size=cfg.B).astype(np.int32)
+
+
+@dataclass
+class StepInputs:
+    """Everything one step consumes, as numpy arrays (bf16 as uint16 bit patterns)."""
+    cfg: Config
+    ctx_len: np.ndarray
+    q: list = field(default_factory=list)        # per layer [B,P,Hq,D]
+    k_blk: list = field(default_factory=list)    # per layer [B,P,Hkv,D]
+    v_blk: list = field(default_factory=list)
+    k_ring: list = field(default_factory=list)   # per layer [B,S,Hkv,D]
+    v_ring: list = field(default_factory=list)
+    conv_x: list = field(default_factory=list)   # per site [B,P,C]
+    conv_base: list = field(default_factory=list)
+    conv_delta: list = field(default_factory=list)
+    draft: np.ndarray | None = None              # [B,P,V]
+    target: np.ndarray | None = None             # [B,P,V]
+    pred_cb: np.ndarray | None = None            # [V,R]
+    succ_cb: np.ndarray | None = None
+    gate: np.ndarray | None = None               # [B,N,R]
+    anchor: np.ndarray | None = None             # [B]
+    temperature: np.ndarray | None = None        # [B]
+
+
+def make_step_inputs(cfg: Config, iset: int = 0, with_attention: bool = True,
+                     with_codebooks: bool = True, cb=None) -> StepInputs:
+    si = StepInputs(cfg=cfg, ctx_len=ctx_len(cfg, iset))
+    if with_attention:
+        for layer in range(cfg.layers):
+            si.q.append(attn_q(cfg, layer, iset=iset))
+            kb, vb = attn_block_kv(cfg, layer, iset=iset)
+            si.k_blk.append(kb)
+            si.v_blk.append(vb)
+            kr, vr = attn_ring(cfg, layer, iset=iset)
+            si.k_ring.append(kr)
+            si.v_ring.append(vr)
+    for site in range(cfg.sites):
+        x, base, delta = conv_inputs(cfg, site, iset=iset)
+        si.conv_x.append(x)
+        si.conv_base.append(base)
+        si.conv_delta.append(delta)
+    si.draft = draft_logits(cfg, iset=iset)
+    si.target = target_rows(cfg, si.draft, iset=iset)
+    if with_codebooks:
+        si.pred_cb, si.succ_cb = cb if cb is not None else codebooks(cfg)
+    si.gate = gate(cfg, iset=iset)
+    si.anchor = anchor(cfg, iset)
+    si.temperature = cfg.temperatures()
+    return si

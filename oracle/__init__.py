@@ -1,0 +1,221 @@
+"""CPU oracle for the DFlash2 block-draft-and-verify step.
+
+TEST INFRASTRUCTURE ONLY. This package wraps ``dflash2_oracle.c``, the plain, slow,
+single-threaded reference that the GPU library is checked against. Only the test suite,
+``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may import it; the
+product path (``block_drafter_draft_amd``) never does, and shares no code with it.
+
+Each wrapper marshals numpy arrays into the C functions; the arithmetic and the citations
+of the pages live in the C file. Functions that are pinned by tests are listed in
+``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dflash2_oracle.c")
+_LIB = os.path.join(_HERE, "libdflash2_oracle.so")
+
+BF16 = 0
+F32 = 1
+
+ST_NONFINITE = 1
+ST_BADTOKEN = 2
+ST_ZEROMASS = 4
+ST_BADPROB = 8
+ST_BADTEMP = 16
+
+K = 16
+
+
+def build() -> str:
+    """Compile the oracle with gcc (no contraction, no fast-math, no vectorised libm)."""
+    cmd = [
+        "gcc", "-std=gnu11", "-O2", "-ffp-contract=off", "-fno-fast-math",
+        "-fno-builtin", "-Wall", "-Wextra", "-Wno-unused-parameter",
+        "-shared", "-fPIC", "-o", _LIB + ".tmp", _SRC, "-lm",
+    ]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        L = ctypes.CDLL(_LIB)
+        vp, i32p, f32p, f64p, u16p, u64p = (ctypes.c_void_p,) * 6
+        c_int, c_i64, c_u64, c_f32, c_f64 = (ctypes.c_int, ctypes.c_int64, ctypes.c_uint64,
+                                             ctypes.c_float, ctypes.c_double)
+        L.or_philox4x64_10.argtypes = [u64p, u64p, u64p]
+        L.or_exp_c.argtypes = [c_f32]
+        L.or_exp_c.restype = c_f32
+        L.or_exp_c_many.argtypes = [f32p, f32p, c_i64]
+        L.or_block_attn.argtypes = [vp, vp, vp, vp, vp, i32p, f64p] + [c_int] * 7 + [c_f64, c_int]
+        L.or_dynconv2.argtypes = [vp, f32p, f32p, f64p] + [c_int] * 5
+        L.or_topk16.argtypes = [vp, c_int, c_int, c_int, c_int, c_i64, c_i64, c_int, i32p, f32p]
+        L.or_viterbi.argtypes = [c_int, c_int, f32p, f32p, i32p]
+        L.or_walk.argtypes = [c_int, c_int, f32p, f32p, c_f32, f32p, i32p, f32p]
+        L.or_select.argtypes = ([i32p, f32p, f32p, u16p, u16p, c_int, c_int, i32p, f32p,
+                                 c_u64, c_u64, c_int, c_int, i32p, i32p, f32p, i32p, f32p])
+        L.or_verify.argtypes = ([vp, c_int, c_i64, c_i64, c_int, i32p, i32p, f32p, i32p, f32p,
+                                 c_u64, c_u64, c_int, c_int, i32p, i32p, i32p])
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray | None):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"expected float32 or bf16 bits (uint16), got {a.dtype}")
+
+
+# ----------------------------------------------------------------------------------------
+# Wrappers
+# ----------------------------------------------------------------------------------------
+
+def philox4x64_10(ctr, key) -> np.ndarray:
+    c = np.ascontiguousarray(np.asarray(ctr, dtype=np.uint64).reshape(4))
+    k = np.ascontiguousarray(np.asarray(key, dtype=np.uint64).reshape(2))
+    out = np.zeros(4, dtype=np.uint64)
+    lib().or_philox4x64_10(_p(c), _p(k), _p(out))
+    return out
+
+
+def exp_c(y: float) -> float:
+    return float(lib().or_exp_c(ctypes.c_float(y)))
+
+
+def exp_c_array(y: np.ndarray) -> np.ndarray:
+    yy = np.ascontiguousarray(y, dtype=np.float32).reshape(-1)
+    out = np.empty_like(yy)
+    lib().or_exp_c_many(_p(yy), _p(out), yy.size)
+    return out.reshape(np.shape(y))
+
+
+def block_attn(q, k_blk, v_blk, k_ring, v_ring, ctx_len, W, scale=None) -> np.ndarray:
+    """Dense binary64 block attention. q [B,P,Hq,D]; blocks [B,P,Hkv,D]; rings [B,S,Hkv,D]."""
+    B, P, Hq, D = q.shape
+    S, Hkv = k_ring.shape[1], k_ring.shape[2]
+    dt = _dtype_code(q)
+    for a in (k_blk, v_blk, k_ring, v_ring):
+        assert _dtype_code(a) == dt
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    arrs = [np.ascontiguousarray(a) for a in (q, k_blk, v_blk, k_ring, v_ring)]
+    cl = np.ascontiguousarray(np.asarray(ctx_len, dtype=np.int32))
+    out = np.zeros((B, P, Hq, D), dtype=np.float64)
+    lib().or_block_attn(*[_p(a) for a in arrs], _p(cl), _p(out), B, P, Hq, Hkv, D, S, W,
+                        float(scale), dt)
+    return out
+
+
+def dynconv2(x, base, delta, group=16) -> np.ndarray:
+    """x [B,P,C] (f32 or bf16 bits); base [2,C] f32; delta [B,P,2,C/group] f32."""
+    B, P, C = x.shape
+    xx = np.ascontiguousarray(x)
+    bb = np.ascontiguousarray(base, dtype=np.float32)
+    dd = np.ascontiguousarray(delta, dtype=np.float32)
+    out = np.zeros((B, P, C), dtype=np.float64)
+    lib().or_dynconv2(_p(xx), _p(bb), _p(dd), _p(out), B, P, C, group, _dtype_code(x))
+    return out
+
+
+def topk16(scores, B, N, row0, seq_stride, row_stride, V):
+    """Top-16 of rows row0..row0+N-1 of each sequence, from a flat buffer with element strides."""
+    s = np.ascontiguousarray(scores).reshape(-1)
+    idx = np.zeros((B, N, K), dtype=np.int32)
+    val = np.zeros((B, N, K), dtype=np.float32)
+    lib().or_topk16(_p(s), _dtype_code(s), B, N, row0, seq_stride, row_stride, V, _p(idx), _p(val))
+    return idx, val
+
+
+def topk16_rows(rows: np.ndarray):
+    """Top-16 of each row of a 2-D array [n, V]."""
+    n, V = rows.shape
+    idx, val = topk16(rows, 1, n, 0, 0, V, V)
+    return idx[0], val[0]
+
+
+def viterbi(s1: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """s1 [K]; s [N-1, K, K] (from candidate kp of slot i-1 to k of slot i)."""
+    Kk = s1.shape[0]
+    N = s.shape[0] + 1
+    a1 = np.ascontiguousarray(s1, dtype=np.float32)
+    a = np.ascontiguousarray(s, dtype=np.float32) if N > 1 else np.zeros(1, np.float32)
+    path = np.zeros(N, dtype=np.int32)
+    lib().or_viterbi(Kk, N, _p(a1), _p(a), _p(path))
+    return path
+
+
+def walk(s1, s, invT: float, uniforms):
+    Kk = s1.shape[0]
+    N = s.shape[0] + 1
+    a1 = np.ascontiguousarray(s1, dtype=np.float32)
+    a = np.ascontiguousarray(s, dtype=np.float32) if N > 1 else np.zeros(1, np.float32)
+    u = np.ascontiguousarray(uniforms, dtype=np.float32)
+    path = np.zeros(N, dtype=np.int32)
+    q = np.zeros((N, Kk), dtype=np.float32)
+    lib().or_walk(Kk, N, _p(a1), _p(a), ctypes.c_float(invT), _p(u), _p(path), _p(q))
+    return path, q
+
+
+def select(cand_idx, cand_val, gate, pred_cb, succ_cb, anchor, temperature, seed, step,
+           want_lattice=False):
+    B, N, _ = cand_idx.shape
+    V, R = pred_cb.shape
+    ci = np.ascontiguousarray(cand_idx, dtype=np.int32)
+    cv = np.ascontiguousarray(cand_val, dtype=np.float32)
+    g = np.ascontiguousarray(gate, dtype=np.float32)
+    A = np.ascontiguousarray(pred_cb, dtype=np.uint16)
+    Bc = np.ascontiguousarray(succ_cb, dtype=np.uint16)
+    an = np.ascontiguousarray(anchor, dtype=np.int32)
+    T = np.ascontiguousarray(temperature, dtype=np.float32)
+    tokens = np.zeros((B, N), np.int32)
+    slot = np.zeros((B, N), np.int32)
+    q = np.zeros((B, N, K), np.float32)
+    status = np.zeros(B, np.int32)
+    lat = np.zeros((B, N, K, K), np.float32) if want_lattice else None
+    lib().or_select(_p(ci), _p(cv), _p(g), _p(A), _p(Bc), V, R, _p(an), _p(T),
+                    ctypes.c_uint64(seed), ctypes.c_uint64(step), B, N, _p(tokens), _p(slot),
+                    _p(q), _p(status), _p(lat))
+    if want_lattice:
+        return tokens, slot, q, status, lat
+    return tokens, slot, q, status
+
+
+def verify(target, B, N, seq_stride, row_stride, V, tokens, cand_idx, q, slot, temperature,
+           seed, step, status=None):
+    """target is a flat (or shaped) f32 / bf16-bits buffer addressed by element strides."""
+    t = np.ascontiguousarray(target).reshape(-1)
+    tok = np.ascontiguousarray(tokens, dtype=np.int32)
+    ci = np.ascontiguousarray(cand_idx, dtype=np.int32)
+    qq = np.ascontiguousarray(q, dtype=np.float32)
+    sl = np.ascontiguousarray(slot, dtype=np.int32)
+    T = np.ascontiguousarray(temperature, dtype=np.float32)
+    n_acc = np.zeros(B, np.int32)
+    out = np.zeros((B, N + 1), np.int32)
+    st = np.zeros(B, np.int32) if status is None else np.ascontiguousarray(status, dtype=np.int32).copy()
+    lib().or_verify(_p(t), _dtype_code(t), seq_stride, row_stride, V, _p(tok), _p(ci), _p(qq),
+                    _p(sl), _p(T), ctypes.c_uint64(seed), ctypes.c_uint64(step), B, N,
+                    _p(n_acc), _p(out), _p(st))
+    return n_acc, out, st
