@@ -1,0 +1,228 @@
+// dflash2_select: the candidate selector ("[Spec Decode] DFlash2: local convolution +
+// candidate selector - #52816", PR description, second item; "Geramy/LSE docs/DFLASH2.md",
+// drafter geometry paragraph: each choice conditioned on its predecessor, top-16
+// candidates, rank-256 codebooks; top-k paragraph: nonfinite scores are rejected).
+//
+// Kernel 1 (grid: slots x sequences, 256 threads): gathers the slot's predecessor rows of
+// the pred codebook (the anchor's for slot 1, else the 16 candidates of the previous slot)
+// and its 16 successor rows of the succ codebook into LDS, then thread (kp, k) evaluates
+// the edge score s(kp -> k) = val[k] + sum_r fl(fl(A[p,r] g[r]) B[c,r]), summed left to
+// right over r in binary32 with no contraction. Scores go to the workspace lattice.
+// Kernel 2 (one wave per sequence): the nonfinite/index checks, then the max-sum path
+// (Viterbi, ties to the lower slot) when greedy, or the inverse-CDF walk with exp_c and
+// Philox uniforms when sampled.
+#include "common.hpp"
+
+namespace df2 {
+namespace {
+
+constexpr int kMaxN = 15;
+constexpr int kMaxR = 512;
+
+__global__ __launch_bounds__(256) void select_lattice_kernel(
+    const int32_t* __restrict__ cidx, const float* __restrict__ cval,
+    const float* __restrict__ gate, const uint16_t* __restrict__ pred_cb,
+    const uint16_t* __restrict__ succ_cb, int V, int R, const int32_t* __restrict__ anchor, int N,
+    float* __restrict__ lattice) {
+  extern __shared__ uint8_t smem[];
+  const int i = blockIdx.x + 1;  // slot 1..N
+  const int b = blockIdx.y;
+  const int t = threadIdx.x;
+  const int kp = t >> 4, k = t & 15;
+  const int RS = R + 2;  // padded row stride in bf16 elements
+  uint16_t* A = reinterpret_cast<uint16_t*>(smem);          // [16][RS]
+  uint16_t* Bm = A + 16 * RS;                               // [16][RS]
+  float* g = reinterpret_cast<float*>(Bm + 16 * RS + 2);    // [R] (4-byte aligned)
+  __shared__ int32_t prow[kTopK], srow[kTopK];
+
+  const int npred = i == 1 ? 1 : kTopK;
+  if (t < kTopK) {
+    int32_t p = i == 1 ? anchor[b] : cidx[((int64_t)b * N + (i - 2)) * kTopK + t];
+    int32_t c = cidx[((int64_t)b * N + (i - 1)) * kTopK + t];
+    prow[t] = (p >= 0 && p < V) ? p : -1;  // invalid indices are never gathered
+    srow[t] = (c >= 0 && c < V) ? c : -1;
+  }
+  __syncthreads();
+  const float* gi = gate + ((int64_t)b * N + (i - 1)) * R;
+  for (int r = t; r < R; r += 256) g[r] = gi[r];
+  for (int e = t; e < npred * R; e += 256) {
+    const int row = e / R, r = e % R;
+    const int32_t p = prow[row];
+    A[row * RS + r] = p >= 0 ? pred_cb[(int64_t)p * R + r] : (uint16_t)0;
+  }
+  for (int e = t; e < kTopK * R; e += 256) {
+    const int row = e / R, r = e % R;
+    const int32_t c = srow[row];
+    Bm[row * RS + r] = c >= 0 ? succ_cb[(int64_t)c * R + r] : (uint16_t)0;
+  }
+  __syncthreads();
+  if (kp >= npred) return;
+  const uint16_t* a = A + kp * RS;
+  const uint16_t* bb = Bm + k * RS;
+  float acc = 0.0f;
+  for (int r = 0; r < R; ++r) {
+    const float ag = __fmul_rn(bf16_to_f32(a[r]), g[r]);
+    const float pr = __fmul_rn(ag, bf16_to_f32(bb[r]));
+    acc = __fadd_rn(acc, pr);
+  }
+  const float v = cval[((int64_t)b * N + (i - 1)) * kTopK + k];
+  lattice[(((int64_t)b * N + (i - 1)) * kTopK + kp) * kTopK + k] = __fadd_rn(v, acc);
+}
+
+__global__ __launch_bounds__(64) void select_path_kernel(
+    const int32_t* __restrict__ cidx, const float* __restrict__ cval, int V,
+    const int32_t* __restrict__ anchor, const float* __restrict__ temperature, uint64_t seed,
+    uint64_t step, int N, const float* __restrict__ lattice, int32_t* __restrict__ tokens,
+    int32_t* __restrict__ slot, float* __restrict__ q, int32_t* __restrict__ status) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  __shared__ float S[kMaxN][kTopK][kTopK];
+  __shared__ int32_t bp[kMaxN][kTopK];
+  __shared__ float dp[kTopK];
+  __shared__ float e_sh[kTopK];
+  __shared__ float uni[kMaxN];
+  __shared__ int32_t path[kMaxN];
+  __shared__ float qout[kMaxN][kTopK];
+
+  // index validity (anchor and every candidate)
+  int bad = 0;
+  if (lane == 0) bad |= !(anchor[b] >= 0 && anchor[b] < V);
+  for (int e = lane; e < N * kTopK; e += 64) {
+    const int32_t c = cidx[(int64_t)b * N * kTopK + e];
+    bad |= !(c >= 0 && c < V);
+  }
+  const bool ok = wave_or(bad) == 0;
+  int st = ok ? 0 : DFLASH2_ST_BADTOKEN;
+
+  // scores into LDS; every computed score and value must be finite
+  int nonfin = 0;
+  if (ok) {
+    for (int e = lane; e < N * kTopK * kTopK; e += 64) {
+      const int i = e / (kTopK * kTopK) + 1, kp = (e / kTopK) % kTopK, k = e % kTopK;
+      const float s = lattice[(int64_t)b * N * kTopK * kTopK + e];
+      S[i - 1][kp][k] = s;
+      if (i == 1 && kp > 0) continue;  // slot 1 has the anchor as its only predecessor
+      const float v = cval[((int64_t)b * N + (i - 1)) * kTopK + k];
+      nonfin |= !(fabsf(s) <= 3.40282347e38f) || !(fabsf(v) <= 3.40282347e38f);
+    }
+  }
+  const bool finite = wave_or(nonfin) == 0;
+  if (ok && !finite) st |= DFLASH2_ST_NONFINITE;
+  float invT = 0.0f;
+  const int mode = temp_mode(temperature[b], &invT, &st);
+
+  int32_t* tk = tokens + (int64_t)b * N;
+  int32_t* sl = slot + (int64_t)b * N;
+  float* qq = q + (int64_t)b * N * kTopK;
+  if (!ok || !finite) {
+    for (int e = lane; e < N * kTopK; e += 64) qq[e] = 0.0f;
+    if (lane < N) {
+      tk[lane] = -1;
+      sl[lane] = -1;
+    }
+    if (lane == 0) status[b] = st;
+    return;
+  }
+  __syncthreads();
+
+  if (mode == 0) {
+    // Viterbi: lane k holds the best prefix score ending at candidate k of the slot
+    if (lane < kTopK) dp[lane] = S[0][0][lane];
+    __syncthreads();
+    for (int i = 2; i <= N; ++i) {
+      float best = 0.0f;
+      int arg = -1;
+      if (lane < kTopK) {
+        for (int kp = 0; kp < kTopK; ++kp) {
+          const float v = __fadd_rn(dp[kp], S[i - 1][kp][lane]);
+          if (arg < 0 || v > best) {
+            best = v;
+            arg = kp;
+          }
+        }
+        bp[i - 1][lane] = arg;
+      }
+      __syncthreads();
+      if (lane < kTopK) dp[lane] = best;
+      __syncthreads();
+    }
+    if (lane == 0) {
+      int last = 0;
+      for (int k = 1; k < kTopK; ++k)
+        if (dp[k] > dp[last]) last = k;
+      path[N - 1] = last;
+      for (int i = N; i >= 2; --i) path[i - 2] = bp[i - 1][path[i - 1]];
+    }
+    __syncthreads();
+    for (int e = lane; e < N * kTopK; e += 64) qq[e] = (e % kTopK) == path[e / kTopK] ? 1.0f : 0.0f;
+  } else {
+    if (lane < N) uni[lane] = uniform24(philox_draw(seed, step, (uint32_t)b, (uint32_t)(lane + 1)).w[0]);
+    __syncthreads();
+    int prev = 0;
+    for (int i = 1; i <= N; ++i) {
+      const int row = i == 1 ? 0 : prev;
+      float s = lane < kTopK ? S[i - 1][row][lane] : -3.40282347e38f;
+      // the maximum is exact in any order
+      float m = s;
+      for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      m = __shfl(m, 0, 64);
+      if (lane < kTopK) e_sh[lane] = exp_c(__fmul_rn(__fsub_rn(s, m), invT));
+      __syncthreads();
+      if (lane == 0) {
+        float Z = 0.0f, C[kTopK];
+        for (int k = 0; k < kTopK; ++k) {
+          Z = __fadd_rn(Z, e_sh[k]);
+          C[k] = Z;
+        }
+        const float tau = __fmul_rn(uni[i - 1], Z);
+        int pick = kTopK - 1;
+        for (int k = 0; k < kTopK; ++k)
+          if (C[k] > tau) {
+            pick = k;
+            break;
+          }
+        path[i - 1] = pick;
+        for (int k = 0; k < kTopK; ++k) qout[i - 1][k] = __fdiv_rn(e_sh[k], Z);
+      }
+      __syncthreads();
+      prev = path[i - 1];
+    }
+    for (int e = lane; e < N * kTopK; e += 64) qq[e] = qout[e / kTopK][e % kTopK];
+  }
+  if (lane < N) {
+    sl[lane] = path[lane];
+    tk[lane] = cidx[((int64_t)b * N + lane) * kTopK + path[lane]];
+  }
+  if (lane == 0) status[b] = st;
+}
+
+}  // namespace
+}  // namespace df2
+
+using namespace df2;
+
+extern "C" size_t dflash2_select_workspace_bytes(int B, int N) {
+  if (B < 1 || N < 1 || N > kMaxN) return 0;
+  return round_up((size_t)B * N * kTopK * kTopK * sizeof(float), kWsAlign);
+}
+
+extern "C" int dflash2_select(const int32_t* cand_idx, const float* cand_val, const float* gate,
+                              const uint16_t* pred_cb, const uint16_t* succ_cb, int V, int R,
+                              const int32_t* anchor, const float* temperature, uint64_t seed,
+                              uint64_t step, int B, int N, int32_t* tokens, int32_t* slot,
+                              float* q, int32_t* status, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  if (!cand_idx || !cand_val || !gate || !pred_cb || !succ_cb || !anchor || !temperature ||
+      !tokens || !slot || !q || !status || !ws)
+    return DFLASH2_EINVAL;
+  if (B < 1 || N < 1 || R < 1 || V < kTopK) return DFLASH2_EINVAL;
+  if (N > kMaxN || R > kMaxR || B > 65535) return DFLASH2_EUNSUPPORTED;
+  if (!aligned(ws, kWsAlign) || ws_bytes < dflash2_select_workspace_bytes(B, N))
+    return DFLASH2_EWORKSPACE;
+  float* lattice = (float*)ws;
+  const size_t lds = (size_t)2 * kTopK * (R + 2) * sizeof(uint16_t) + 4 + (size_t)R * sizeof(float);
+  select_lattice_kernel<<<dim3(N, B), 256, lds, stream>>>(cand_idx, cand_val, gate, pred_cb, succ_cb,
+                                                         V, R, anchor, N, lattice);
+  select_path_kernel<<<B, 64, 0, stream>>>(cand_idx, cand_val, V, anchor, temperature, seed, step,
+                                           N, lattice, tokens, slot, q, status);
+  return launch_status();
+}

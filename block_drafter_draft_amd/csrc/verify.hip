@@ -1,0 +1,511 @@
+// dflash2_verify: target verification of the N proposals ("Geramy/LSE docs/DFLASH2.md",
+// usage paragraph: probability-ratio rejection with residual sampling over all seven
+// proposals, greedy keeps the deterministic chain; drafter-geometry paragraph: the target
+// consumes the anchor plus all proposals, so an all-accept step has a bonus row).
+//
+// Kernel 1 (grid: chunks x sequences) reads each needed target row chunk once:
+//   greedy  - rows 0..N: the chunk's first element under the top-16 order (packed word);
+//   sampled - the accept chain is cheap (N gathers and N Philox draws, one per lane), so
+//             every workgroup of the sequence recomputes it and then reads only the row it
+//             will draw from: the chunk sums of the integer weights floor(w * 2^40), both
+//             for p_t itself and with the 16 candidates' residual max(0, p_t - q) swapped in.
+// Kernel 2 (one workgroup per sequence) runs the greedy chain on the row maxima, or picks
+// the chunk holding the draw from the chunk sums and scans that one chunk in index order.
+// Integer weights make the draw independent of the summation order, so it is bit-exact.
+#include "common.hpp"
+
+namespace df2 {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxN = 15;
+
+struct ChainRec {
+  int32_t n_acc;   // accepted proposals
+  int32_t pos;     // block position of the drawn token (1..N+1)
+  int32_t resid;   // 1: draw from the residual of slot pos; 0: from p_t itself
+  int32_t flags;   // status bits from the accept tests
+};
+
+struct Ws {
+  ChainRec* chain;   // [B]
+  uint64_t* best;    // [B][N+1][nchunks] greedy chunk maxima
+  uint64_t* zsum;    // [B][nchunks][2] sampled chunk sums (residual, plain)
+  int32_t* zflag;    // [B][nchunks] status bits seen in the chunk
+};
+
+__host__ __device__ inline size_t ws_layout(int B, int N, int nchunks, Ws* w, char* base) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = (off + bytes + 255) / 256 * 256;
+    return o;
+  };
+  size_t o_chain = take(sizeof(ChainRec) * B);
+  size_t o_best = take(sizeof(uint64_t) * (size_t)B * (N + 1) * nchunks);
+  size_t o_z = take(sizeof(uint64_t) * 2 * (size_t)B * nchunks);
+  size_t o_f = take(sizeof(int32_t) * (size_t)B * nchunks);
+  if (w && base) {
+    w->chain = (ChainRec*)(base + o_chain);
+    w->best = (uint64_t*)(base + o_best);
+    w->zsum = (uint64_t*)(base + o_z);
+    w->zflag = (int32_t*)(base + o_f);
+  }
+  return off;
+}
+
+template <class KT>
+__device__ __forceinline__ uint32_t load_bits(const typename KT::elem_t* p, int64_t i) {
+  if constexpr (sizeof(typename KT::elem_t) == 2)
+    return reinterpret_cast<const uint16_t*>(p)[i];
+  else
+    return __float_as_uint(reinterpret_cast<const float*>(p)[i]);
+}
+
+// Accept chain of a sampled sequence, computed by wave 0 (lane j-1 tests proposal j) and
+// published in *rec (LDS). All threads must call; returns after a barrier.
+__device__ void accept_chain(const float* __restrict__ tgt, int64_t row_stride, int V, int N,
+                             const int32_t* __restrict__ tokens, const int32_t* __restrict__ cidx,
+                             const float* __restrict__ q, const int32_t* __restrict__ slot,
+                             uint64_t seed, uint64_t step, int b, ChainRec* rec) {
+  const int t = threadIdx.x;
+  if (t < 64) {
+    bool acc = false, plain = false;
+    int fl = 0;
+    if (t < N) {
+      const int j = t + 1;
+      const int32_t x = tokens[(int64_t)b * N + t];
+      Draw d = philox_draw(seed, step, (uint32_t)b, (uint32_t)j);
+      const float u = uniform24(d.w[1]);
+      if (x < 0 || x >= V) {
+        plain = true;
+      } else {
+        const int32_t sl = slot[(int64_t)b * N + t];
+        const int32_t* ci = cidx + ((int64_t)b * N + t) * kTopK;
+        if (sl < 0 || sl >= kTopK || ci[sl] != x) {
+          fl |= DFLASH2_ST_BADTOKEN;
+          plain = true;
+        } else {
+          const float qx = prob_ok(q[((int64_t)b * N + t) * kTopK + sl], &fl);
+          const float pt = prob_ok(tgt[(int64_t)t * row_stride + x], &fl);
+          acc = __fmul_rn(u, qx) < pt;
+        }
+      }
+    }
+    const uint64_t rej = __ballot(t < N && !acc);
+    const int first = rej ? __ffsll((unsigned long long)rej) - 1 : N;  // lane of the rejection
+    const int use = (t < N && t <= first) ? fl : 0;
+    const int flags = wave_or(use);
+    const int plain_first = __shfl(plain ? 1 : 0, first < N ? first : 0, 64);
+    if (t == 0) {
+      rec->n_acc = first;
+      rec->pos = first + 1;
+      rec->resid = (first < N && !plain_first) ? 1 : 0;
+      rec->flags = flags;
+    }
+  }
+  __syncthreads();
+}
+
+template <class KT, int EPT>
+__global__ __launch_bounds__(kThreads) void verify_rows_kernel(
+    const typename KT::elem_t* __restrict__ target, int64_t seq_stride, int64_t row_stride, int V,
+    const int32_t* __restrict__ tokens, const int32_t* __restrict__ cidx,
+    const float* __restrict__ q, const int32_t* __restrict__ slot,
+    const float* __restrict__ temperature, uint64_t seed, uint64_t step, int N, int nchunks,
+    Ws ws) {
+  constexpr int CH = EPT * kThreads;
+  const int chunk = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  const int base = chunk * CH;
+  __shared__ ChainRec rec;
+  __shared__ uint64_t red[kThreads / 64][2];
+  __shared__ int redf[kThreads / 64];
+
+  int st = 0;
+  float invT = 0.0f;
+  int mode = temp_mode(temperature[b], &invT, &st);
+  constexpr bool kIsF32 = sizeof(typename KT::elem_t) == 4;
+  if (!kIsF32) mode = 0;
+  const typename KT::elem_t* tb = target + (int64_t)b * seq_stride;
+
+  if (mode == 0) {
+    // greedy: chunk maximum of every row (elements visited in increasing index per thread)
+    for (int r = 0; r <= N; ++r) {
+      const typename KT::elem_t* row = tb + (int64_t)r * row_stride;
+      uint32_t bk = 0, bi = 0;
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        const int x = base + t * EPT + e;
+        if (x < V) {
+          const uint32_t k = KT::canon(load_bits<KT>(row, x));
+          if (k > bk) {
+            bk = k;
+            bi = (uint32_t)x;
+          }
+        }
+      }
+      uint64_t m = bk ? pack_cand(bk, bi) : 0ull;
+      m = wave_max_u64(m);
+      if ((t & 63) == 0) red[t >> 6][0] = m;
+      __syncthreads();
+      if (t == 0) {
+        uint64_t g = red[0][0];
+        for (int w = 1; w < kThreads / 64; ++w) g = red[w][0] > g ? red[w][0] : g;
+        ws.best[((int64_t)b * (N + 1) + r) * nchunks + chunk] = g;
+      }
+      __syncthreads();
+    }
+    return;
+  }
+
+  // sampled: which row, and with which candidate corrections
+  const float* tgt = reinterpret_cast<const float*>(tb);
+  accept_chain(tgt, row_stride, V, N, tokens, cidx, q, slot, seed, step, b, &rec);
+  if (chunk == 0 && t == 0) ws.chain[b] = rec;
+  const float* row = tgt + (int64_t)(rec.pos - 1) * row_stride;
+
+  uint64_t zp = 0;
+  int fl = 0;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int x = base + t * EPT + e;
+    if (x < V) zp += quant40(prob_ok(row[x], &fl));
+  }
+  // residual corrections for the candidates of slot pos that fall in this chunk; for a
+  // repeated index only its first occurrence counts
+  int64_t dz = 0;
+  if (rec.resid && t < kTopK) {
+    const int32_t* ci = cidx + ((int64_t)b * N + (rec.pos - 1)) * kTopK;
+    const float* qr = q + ((int64_t)b * N + (rec.pos - 1)) * kTopK;
+    const int32_t c = ci[t];
+    bool first = c >= 0 && c < V;
+    for (int k = 0; k < t; ++k) first = first && ci[k] != c;
+    if (first && c >= base && c < base + CH) {
+      int dummy = 0;
+      const float p = prob_ok(row[c], &dummy);
+      const float qk = prob_ok(qr[t], &fl);
+      const float d = __fsub_rn(p, qk);
+      dz = (int64_t)quant40(d > 0.0f ? d : 0.0f) - (int64_t)quant40(p);
+    }
+  }
+  uint64_t zr = zp + (uint64_t)dz;
+  zp = wave_sum_u64(zp);
+  zr = wave_sum_u64(zr);
+  fl = wave_or(fl);
+  if ((t & 63) == 0) {
+    red[t >> 6][0] = zr;
+    red[t >> 6][1] = zp;
+    redf[t >> 6] = fl;
+  }
+  __syncthreads();
+  if (t == 0) {
+    uint64_t a = 0, c = 0;
+    int f = 0;
+    for (int w = 0; w < kThreads / 64; ++w) {
+      a += red[w][0];
+      c += red[w][1];
+      f |= redf[w];
+    }
+    ws.zsum[((int64_t)b * nchunks + chunk) * 2 + 0] = a;
+    ws.zsum[((int64_t)b * nchunks + chunk) * 2 + 1] = c;
+    ws.zflag[(int64_t)b * nchunks + chunk] = f;
+  }
+}
+
+// inclusive scan of a u64 over the workgroup (all threads call)
+__device__ __forceinline__ uint64_t block_incl_scan_u64(uint64_t v, uint64_t* wsum) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    uint32_t lo = __shfl_up((uint32_t)v, d, 64), hi = __shfl_up((uint32_t)(v >> 32), d, 64);
+    uint64_t o = ((uint64_t)hi << 32) | lo;
+    if (lane >= d) v += o;
+  }
+  if (lane == 63) wsum[w] = v;
+  __syncthreads();
+  uint64_t add = 0;
+  for (int i = 0; i < w; ++i) add += wsum[i];
+  __syncthreads();
+  return v + add;
+}
+
+template <class KT, int EPT>
+__global__ __launch_bounds__(kThreads) void verify_finish_kernel(
+    const typename KT::elem_t* __restrict__ target, int64_t seq_stride, int64_t row_stride, int V,
+    const int32_t* __restrict__ tokens, const int32_t* __restrict__ cidx,
+    const float* __restrict__ q, const float* __restrict__ temperature, uint64_t seed,
+    uint64_t step, int N, int nchunks, Ws ws, int32_t* __restrict__ n_accept,
+    int32_t* __restrict__ out_tokens, int32_t* __restrict__ status) {
+  constexpr int CH = EPT * kThreads;
+  const int b = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  __shared__ uint64_t rowbest[kMaxN + 1];
+  __shared__ uint64_t wsum[kThreads / 64];
+  __shared__ uint64_t sh_z[2];
+  __shared__ int sh_f[kThreads / 64];
+  __shared__ int sh_chunk;
+  __shared__ uint64_t sh_tau;
+  __shared__ int sh_tok;
+  __shared__ int32_t cand[kTopK];
+  __shared__ float candq[kTopK];
+
+  int st = 0;
+  float invT = 0.0f;
+  int mode = temp_mode(temperature[b], &invT, &st);
+  constexpr bool kIsF32 = sizeof(typename KT::elem_t) == 4;
+  if (mode == 1 && !kIsF32) {
+    st |= DFLASH2_ST_BADPROB;
+    mode = 0;
+  }
+  const int32_t* d = tokens + (int64_t)b * N;
+  int32_t* out = out_tokens + (int64_t)b * (N + 1);
+  const typename KT::elem_t* tb = target + (int64_t)b * seq_stride;
+
+  if (mode == 0) {
+    for (int r = w; r <= N; r += kThreads / 64) {
+      uint64_t m = 0;
+      const uint64_t* src = ws.best + ((int64_t)b * (N + 1) + r) * nchunks;
+      for (int c = lane; c < nchunks; c += 64) m = src[c] > m ? src[c] : m;
+      m = wave_max_u64(m);
+      if (lane == 0) rowbest[r] = m;
+    }
+    __syncthreads();
+    if (t == 0) {
+      int n = 0;
+      int32_t emitted = -1;
+      for (int j = 1; j <= N + 1; ++j) {
+        const uint64_t m = rowbest[j - 1];
+        const int32_t y = (int32_t)cand_idx(m);
+        if (cand_key(m) == KT::kNaN) st |= DFLASH2_ST_NONFINITE;
+        if (j <= N && d[j - 1] == y) {
+          ++n;
+          continue;
+        }
+        emitted = y;
+        break;
+      }
+      for (int j = 0; j <= N; ++j) out[j] = j < n ? d[j] : (j == n ? emitted : -1);
+      n_accept[b] = n;
+      status[b] |= st;
+    }
+    return;
+  }
+
+  // sampled
+  const ChainRec rec = ws.chain[b];
+  st |= rec.flags;
+  const float* row = reinterpret_cast<const float*>(tb) + (int64_t)(rec.pos - 1) * row_stride;
+  {
+    uint64_t zr = 0, zp = 0;
+    int f = 0;
+    for (int c = t; c < nchunks; c += kThreads) {
+      zr += ws.zsum[((int64_t)b * nchunks + c) * 2 + 0];
+      zp += ws.zsum[((int64_t)b * nchunks + c) * 2 + 1];
+      f |= ws.zflag[(int64_t)b * nchunks + c];
+    }
+    zr = wave_sum_u64(zr);
+    zp = wave_sum_u64(zp);
+    f = wave_or(f);
+    if (lane == 0) {
+      wsum[w] = zr;
+      sh_f[w] = f;
+    }
+    __syncthreads();
+    if (t == 0) {
+      uint64_t a = 0;
+      int ff = 0;
+      for (int i = 0; i < kThreads / 64; ++i) {
+        a += wsum[i];
+        ff |= sh_f[i];
+      }
+      sh_z[0] = a;
+      sh_f[0] = ff;
+    }
+    __syncthreads();
+    if (lane == 0) wsum[w] = zp;
+    __syncthreads();
+    if (t == 0) {
+      uint64_t a = 0;
+      for (int i = 0; i < kThreads / 64; ++i) a += wsum[i];
+      sh_z[1] = a;
+    }
+    __syncthreads();
+  }
+  st |= sh_f[0];
+  int use_resid = rec.resid;
+  uint64_t Z = use_resid ? sh_z[0] : sh_z[1];
+  if (Z == 0 && use_resid) {
+    use_resid = 0;
+    Z = sh_z[1];
+  }
+  if (t < kTopK) {
+    if (use_resid) {
+      cand[t] = cidx[((int64_t)b * N + (rec.pos - 1)) * kTopK + t];
+      candq[t] = q[((int64_t)b * N + (rec.pos - 1)) * kTopK + t];
+    } else {
+      cand[t] = -1;
+      candq[t] = 0.0f;
+    }
+  }
+  int32_t emitted = -1;
+  if (Z == 0) {
+    // no mass at all: the row's first element under the top-16 order
+    st |= DFLASH2_ST_ZEROMASS;
+    uint32_t bk = 0, bi = 0;
+    for (int x = t; x < V; x += kThreads) {
+      const uint32_t k = KeyF32::canon(__float_as_uint(row[x]));
+      if (k > bk) {
+        bk = k;
+        bi = (uint32_t)x;
+      }
+    }
+    uint64_t m = bk ? pack_cand(bk, bi) : 0ull;
+    m = wave_max_u64(m);
+    if (lane == 0) wsum[w] = m;
+    __syncthreads();
+    if (t == 0) {
+      uint64_t g = wsum[0];
+      for (int i = 1; i < kThreads / 64; ++i) g = wsum[i] > g ? wsum[i] : g;
+      sh_tok = (int)cand_idx(g);
+    }
+    __syncthreads();
+    emitted = sh_tok;
+  } else {
+    if (t == 0) {
+      sh_tok = -1;
+      const Draw dr = philox_draw(seed, step, (uint32_t)b, (uint32_t)rec.pos);
+      const uint64_t tau = scale_draw(dr.w[2], Z);
+      uint64_t cum = 0;
+      int c = 0;
+      for (; c < nchunks; ++c) {
+        const uint64_t zc = ws.zsum[((int64_t)b * nchunks + c) * 2 + (use_resid ? 0 : 1)];
+        if (cum + zc > tau) break;
+        cum += zc;
+      }
+      sh_chunk = c;
+      sh_tau = tau - cum;
+    }
+    __syncthreads();
+    // scan the chosen chunk in index order: thread t owns EPT consecutive elements
+    const int c0 = sh_chunk * CH + t * EPT;
+    uint64_t wgt[EPT];
+    uint64_t mine = 0;
+    int dummy = 0;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int x = c0 + e;
+      uint64_t r = 0;
+      if (x < V) {
+        const float p = prob_ok(row[x], &dummy);
+        r = quant40(p);
+        for (int k = 0; k < kTopK; ++k) {
+          if (cand[k] == x) {
+            const float qk = prob_ok(candq[k], &dummy);
+            const float df = __fsub_rn(p, qk);
+            r = quant40(df > 0.0f ? df : 0.0f);
+            break;
+          }
+        }
+      }
+      wgt[e] = r;
+      mine += r;
+    }
+    const uint64_t incl = block_incl_scan_u64(mine, wsum);
+    const uint64_t excl = incl - mine;
+    const uint64_t tau = sh_tau;
+    if (excl <= tau && tau < incl) {
+      uint64_t run = excl;
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        run += wgt[e];
+        if (run > tau) {
+          sh_tok = c0 + e;
+          break;
+        }
+      }
+    }
+    __syncthreads();
+    emitted = sh_tok;
+  }
+  if (t == 0) {
+    const int n = rec.n_acc;
+    for (int j = 0; j <= N; ++j) out[j] = j < n ? d[j] : (j == n ? emitted : -1);
+    n_accept[b] = n;
+    status[b] |= st;
+  }
+}
+
+struct Plan {
+  int ept;
+  int nchunks;
+};
+
+Plan make_plan(int B, int V) {
+  Plan p;
+  int ept = 16;
+  while (ept > 4 && (int64_t)B * ((V + ept * kThreads - 1) / (ept * kThreads)) < 512) ept >>= 1;
+  p.ept = ept;
+  p.nchunks = (V + ept * kThreads - 1) / (ept * kThreads);
+  return p;
+}
+
+template <class KT, int EPT>
+void launch(const Plan& p, const void* target, int64_t ss, int64_t rs, int V,
+            const int32_t* tokens, const int32_t* cidx, const float* q, const int32_t* slot,
+            const float* temp, uint64_t seed, uint64_t step, int B, int N, Ws w, int32_t* n_acc,
+            int32_t* out, int32_t* status, hipStream_t st) {
+  using E = typename KT::elem_t;
+  verify_rows_kernel<KT, EPT><<<dim3(p.nchunks, B), kThreads, 0, st>>>(
+      (const E*)target, ss, rs, V, tokens, cidx, q, slot, temp, seed, step, N, p.nchunks, w);
+  verify_finish_kernel<KT, EPT><<<B, kThreads, 0, st>>>((const E*)target, ss, rs, V, tokens, cidx,
+                                                        q, temp, seed, step, N, p.nchunks, w,
+                                                        n_acc, out, status);
+}
+
+template <class KT>
+void launch_ept(const Plan& p, const void* target, int64_t ss, int64_t rs, int V,
+                const int32_t* tokens, const int32_t* cidx, const float* q, const int32_t* slot,
+                const float* temp, uint64_t seed, uint64_t step, int B, int N, Ws w,
+                int32_t* n_acc, int32_t* out, int32_t* status, hipStream_t st) {
+  switch (p.ept) {
+    case 16: launch<KT, 16>(p, target, ss, rs, V, tokens, cidx, q, slot, temp, seed, step, B, N, w, n_acc, out, status, st); break;
+    case 8: launch<KT, 8>(p, target, ss, rs, V, tokens, cidx, q, slot, temp, seed, step, B, N, w, n_acc, out, status, st); break;
+    default: launch<KT, 4>(p, target, ss, rs, V, tokens, cidx, q, slot, temp, seed, step, B, N, w, n_acc, out, status, st); break;
+  }
+}
+
+}  // namespace
+}  // namespace df2
+
+using namespace df2;
+
+extern "C" size_t dflash2_verify_workspace_bytes(int B, int N, int V, int dtype) {
+  if (B < 1 || N < 1 || N > kMaxN || V < kTopK) return 0;
+  (void)dtype;
+  Plan p = make_plan(B, V);
+  return ws_layout(B, N, p.nchunks, nullptr, nullptr);
+}
+
+extern "C" int dflash2_verify(const void* target, int dtype, int64_t seq_stride, int64_t row_stride,
+                              int V, const int32_t* tokens, const int32_t* cand_idx, const float* q,
+                              const int32_t* slot, const float* temperature, uint64_t seed,
+                              uint64_t step, int B, int N, int32_t* n_accept, int32_t* out_tokens,
+                              int32_t* status, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!target || !tokens || !cand_idx || !q || !slot || !temperature || !n_accept ||
+      !out_tokens || !status || !ws)
+    return DFLASH2_EINVAL;
+  if (B < 1 || N < 1 || V < kTopK || seq_stride < 0 || row_stride < 0) return DFLASH2_EINVAL;
+  if (N > kMaxN || B > 65535) return DFLASH2_EUNSUPPORTED;
+  if (dtype != DFLASH2_BF16 && dtype != DFLASH2_F32) return DFLASH2_EUNSUPPORTED;
+  if (!aligned(ws, kWsAlign) || ws_bytes < dflash2_verify_workspace_bytes(B, N, V, dtype))
+    return DFLASH2_EWORKSPACE;
+  Plan p = make_plan(B, V);
+  Ws w;
+  ws_layout(B, N, p.nchunks, &w, (char*)ws);
+  if (dtype == DFLASH2_BF16)
+    launch_ept<KeyBF16>(p, target, seq_stride, row_stride, V, tokens, cand_idx, q, slot,
+                        temperature, seed, step, B, N, w, n_accept, out_tokens, status, stream);
+  else
+    launch_ept<KeyF32>(p, target, seq_stride, row_stride, V, tokens, cand_idx, q, slot,
+                       temperature, seed, step, B, N, w, n_accept, out_tokens, status, stream);
+  return launch_status();
+}

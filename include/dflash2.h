@@ -1,0 +1,208 @@
+/*
+ * dflash2.h - C ABI of the DFlash2 block-draft-and-verify step for AMD Instinct MI355X
+ * (gfx950). Library: libdflash2.so.
+ *
+ * One draft-and-verify step of a DFlash2 drafter has five stages, each a call below:
+ * block attention and the two-tap dynamic convolution inside the drafter's layers,
+ * top-16 candidate extraction per block position, the predecessor-conditioned selector,
+ * and target verification. The computation is the one described on these pages:
+ *   - "Geramy/LSE docs/DFLASH2.md": drafter geometry paragraph (block of eight = anchor
+ *     plus seven masks, noncausal block attention, 2048-position context window, two-tap
+ *     conv with groups of 16, top-16 candidates, rank-256 codebooks); usage paragraph
+ *     (verification of all seven proposals by probability-ratio rejection with residual
+ *     sampling, deterministic greedy selection); top-k policy paragraph (ties to the
+ *     smaller index, NaNs first by index, infinities ordered normally).
+ *   - "[Spec Decode] DFlash2: local convolution + candidate selector - #52816": the PR
+ *     description's conv formula and selector edge score, best path from the verified
+ *     anchor, inverse-CDF walk returning q for the lossless verify.
+ *   - "qwen35: DSpark speculative decoding (Qwen3.8-27B drafters) - #625": the DFlash 2
+ *     commit message (two taps over the block, per-element base plus per-group dynamic
+ *     coefficient; top-k, codebook gathers and path search).
+ *
+ * Conventions (all calls):
+ *   - Every array pointer is DEVICE memory owned by the caller, and must stay valid until
+ *     the work enqueued on `stream` has completed. The library allocates nothing, keeps no
+ *     mutable global state (calls are thread-safe), never synchronises and never falls
+ *     back to the host.
+ *   - Calls enqueue kernels on `stream` (0 = the null stream) and return at once. The
+ *     return value reports argument errors known on the host (DFLASH2_E*); nothing is
+ *     launched when it is nonzero. Data-dependent problems are reported per sequence in
+ *     the device array `status` (DFLASH2_ST_* bits).
+ *   - bf16 arrays hold 16-bit patterns (the upper half of an IEEE binary32). Element
+ *     strides are in elements, not bytes.
+ *   - Scratch memory is passed as `ws`/`ws_bytes`; the sizes come from the
+ *     *_workspace_bytes functions. It must be 256-byte aligned. Its contents between
+ *     calls do not matter, and two calls in flight at once must not share it.
+ *   - Random draws come from Philox4x64-10 (Salmon et al., SC'11) with key (seed, 0) and
+ *     counter (step, b, j, 0), for sequence b and block position j. Word 0 drives the
+ *     selector walk at slot j, word 1 the accept test of proposal j, word 2 the residual
+ *     or bonus draw of the token emitted at position j.
+ */
+#ifndef DFLASH2_H
+#define DFLASH2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+#define DFLASH2_BF16 0
+#define DFLASH2_F32 1
+
+/* return codes */
+#define DFLASH2_OK 0
+#define DFLASH2_EINVAL (-1)       /* null pointer, bad size or inconsistent shape */
+#define DFLASH2_EUNSUPPORTED (-2) /* a shape or type this build does not implement */
+#define DFLASH2_EWORKSPACE (-3)   /* ws too small or misaligned */
+#define DFLASH2_EHIP (-4)         /* a kernel launch failed */
+
+/* per-sequence status bits (device int32, OR-ed) */
+#define DFLASH2_ST_NONFINITE 1 /* a NaN/inf selector score, or a NaN chosen by the greedy chain */
+#define DFLASH2_ST_BADTOKEN 2  /* a candidate/anchor index out of range, or a proposal whose slot
+                                  does not match its candidate */
+#define DFLASH2_ST_ZEROMASS 4  /* the sampling row had no mass; its first element was emitted */
+#define DFLASH2_ST_BADPROB 8   /* a probability outside [0, 1] or NaN (taken as 0), or sampling
+                                  requested on a bf16 target (the greedy chain was used) */
+#define DFLASH2_ST_BADTEMP 16  /* a temperature that is negative, NaN, infinite or whose
+                                  reciprocal overflows (treated as greedy) */
+
+/* Temperature classes (select and verify): T == 0 selects greedy; T > 0 and finite with a
+ * finite binary32 1/T selects sampling; anything else sets ST_BADTEMP and is greedy. */
+
+/*
+ * dflash2_block_attn - attention of the P block positions over their windowed context and
+ * the whole block ("Geramy/LSE docs/DFLASH2.md", drafter geometry paragraph).
+ *
+ *   q      [B, P, Hq, D]    queries (after any rotary embedding)
+ *   k_blk, v_blk [B, P, Hkv, D]  keys/values of the P block positions
+ *   k_ring, v_ring [B, S, Hkv, D] context keys/values; context position j of sequence b
+ *                            lives in row j mod S
+ *   ctx_len [B] int32       L_b, the number of context positions (>= 0)
+ *   out    [B, P, Hq, D]    result, same dtype as q
+ *
+ * Slot i of sequence b sits at absolute position L_b + i. It attends to every block key
+ * (noncausal inside the block) and to context positions j with L_b + i - j < W and
+ * 0 <= j < L_b. Query head h uses KV head h / (Hq / Hkv). Scores are scaled by `scale`
+ * (pass 1/sqrt(D) for the usual scaling), softmax in binary32.
+ * dtype: DFLASH2_BF16 (MFMA path) or DFLASH2_F32, for all of q, k*, v*, out.
+ * Requires B >= 1, 2 <= P <= 16, Hq % Hkv == 0, (Hq / Hkv) * P <= 32 for bf16 (64 for
+ * f32), D in {64, 128}, W >= 1, S >= W - 1 (every windowed key is still in the ring),
+ * and ctx_len[b] >= 0 (negative values are clamped to 0 on the device).
+ * Workspace: dflash2_block_attn_workspace_bytes.
+ */
+int dflash2_block_attn(const void *q, const void *k_blk, const void *v_blk, const void *k_ring,
+                       const void *v_ring, const int32_t *ctx_len, void *out, int B, int P, int Hq,
+                       int Hkv, int D, int S, int W, float scale, int dtype, void *ws,
+                       size_t ws_bytes, hipStream_t stream);
+size_t dflash2_block_attn_workspace_bytes(int B, int P, int Hq, int Hkv, int D, int S, int W,
+                                          int dtype);
+
+/*
+ * dflash2_dynconv2 - grouped dynamic two-tap convolution over the block ("[Spec Decode]
+ * DFlash2: local convolution + candidate selector - #52816", PR description, first item):
+ *
+ *   out[b,i,c] = (base[0,c] + delta[b,i,0,c/group]) * x[b,i,c]
+ *              + (base[1,c] + delta[b,i,1,c/group]) * x[b,i-1,c],   x[b,-1,c] = 0
+ *
+ *   x, out [B, P, C] (dtype), base [2, C] f32, delta [B, P, 2, C/group] f32.
+ * Arithmetic in binary32, each product and sum rounded once, result rounded to dtype.
+ * Requires group == 16 and C % 16 == 0, P in [1, 16]. No workspace. out may not alias x.
+ */
+int dflash2_dynconv2(const void *x, const float *base, const float *delta, void *out, int B, int P,
+                     int C, int group, int dtype, hipStream_t stream);
+
+/*
+ * dflash2_topk16 - the 16 first elements of each logits row under the order: every NaN
+ * (by ascending index), then +inf, finite values descending, -inf; equal values (and -0,
+ * +0) by ascending index ("Geramy/LSE docs/DFLASH2.md", top-k policy paragraph).
+ *
+ *   scores  rows addressed as scores[b*seq_stride + (row0 + r)*row_stride + x], r < N, x < V
+ *   idx     [B, N, 16] int32 (best first); val [B, N, 16] f32 (the element, widened)
+ * Requires V >= 16, N >= 1, row0 >= 0, strides >= 0, B*N <= 65535, V <= 8388608.
+ * Workspace: dflash2_topk16_workspace_bytes.
+ */
+int dflash2_topk16(const void *scores, int dtype, int B, int N, int row0, int64_t seq_stride,
+                   int64_t row_stride, int V, int32_t *idx, float *val, void *ws, size_t ws_bytes,
+                   hipStream_t stream);
+size_t dflash2_topk16_workspace_bytes(int B, int N, int V, int dtype);
+
+/*
+ * dflash2_select - the candidate selector ("[Spec Decode] DFlash2: local convolution +
+ * candidate selector - #52816", PR description, second item).
+ *
+ * Edge score from candidate p of slot i-1 (the anchor for slot 1) to candidate c of slot i:
+ *   s_i(p, c) = cand_val[b,i-1,c] + sum_r pred_cb[p,r] * gate[b,i-1,r] * succ_cb[c,r]
+ * evaluated in binary32 as fl(fl(pred*gate)*succ) summed left to right over r, then the
+ * candidate's value added. Any NaN/inf score or value sets ST_NONFINITE; any index outside
+ * [0, V) sets ST_BADTOKEN; such sequences get tokens = slot = -1 and q = 0.
+ * Greedy (T == 0): the max-sum path (Viterbi; ties to the lower candidate slot, the last
+ * slot decided first), q one-hot at the chosen slot.
+ * Sampled (T > 0): for i = 1..N, with prev the previous choice: e_k = exp_c((s_k - max)/T)
+ * (exp_c: a fixed binary32 exp by Cody-Waite reduction and a degree-7 Taylor polynomial),
+ * Z and running sums accumulated in k order, tau = u*Z with u the walk uniform of (b, i),
+ * choice = the first k whose running sum exceeds tau, q_i[k] = e_k / Z.
+ *
+ *   cand_idx, cand_val [B, N, 16] (from dflash2_topk16); gate [B, N, R] f32;
+ *   pred_cb, succ_cb [V, R] bf16; anchor [B] int32; temperature [B] f32;
+ *   tokens, slot [B, N] int32; q [B, N, 16] f32; status [B] int32 (overwritten).
+ * Requires 1 <= N <= 15, 1 <= R <= 512, V >= 16, B <= 65535.
+ * Workspace: dflash2_select_workspace_bytes.
+ */
+int dflash2_select(const int32_t *cand_idx, const float *cand_val, const float *gate,
+                   const uint16_t *pred_cb, const uint16_t *succ_cb, int V, int R,
+                   const int32_t *anchor, const float *temperature, uint64_t seed, uint64_t step,
+                   int B, int N, int32_t *tokens, int32_t *slot, float *q, int32_t *status,
+                   void *ws, size_t ws_bytes, hipStream_t stream);
+size_t dflash2_select_workspace_bytes(int B, int N);
+
+/*
+ * dflash2_verify - target verification of the N proposals ("Geramy/LSE docs/DFLASH2.md",
+ * usage and drafter-geometry paragraphs: probability-ratio rejection with residual
+ * sampling, the target consumes the anchor plus all proposals, greedy keeps the
+ * deterministic chain).
+ *
+ * target rows r = 0..N of sequence b at target[b*seq_stride + r*row_stride + x]; row j-1
+ * verifies proposal j and row N follows the last proposal.
+ * Greedy (T == 0; target may be bf16 or f32 logits/probabilities): y_j = the first element
+ * of row j-1 under the top-16 order; proposals are accepted while tokens[j-1] == y_j, then
+ * y at the first mismatch (or the first element of row N) is emitted. A NaN chosen this
+ * way sets ST_NONFINITE.
+ * Sampled (T > 0; target must be f32 probabilities): proposal j is accepted iff
+ * u * q[b,j-1,slot] < p_t(token), u the accept uniform of (b, j). At the first rejection
+ * the token is drawn from max(0, p_t - q_j) over the whole vocabulary (q_j is zero off the
+ * 16 candidates; the first of duplicated candidates counts); if all N are accepted the
+ * bonus token is drawn from row N. Each weight is quantised to floor(w * 2^40); the token
+ * is the first x whose running integer sum exceeds floor(word2 * Z / 2^64). Zero residual
+ * mass falls back to p_t; zero p_t mass emits the row's first element (ST_ZEROMASS).
+ * A proposal outside [0, V) is a rejection; one whose slot/candidate does not match sets
+ * ST_BADTOKEN and is rejected with q taken as 0.
+ *
+ *   tokens, slot [B, N] int32; cand_idx [B, N, 16] int32; q [B, N, 16] f32;
+ *   temperature [B] f32; n_accept [B] int32; out_tokens [B, N+1] int32 (accepted proposals,
+ *   then the emitted token, then -1); status [B] int32 (OR-ed, not cleared).
+ * Requires 1 <= N <= 15, V >= 16, strides >= 0.
+ * Workspace: dflash2_verify_workspace_bytes.
+ */
+int dflash2_verify(const void *target, int dtype, int64_t seq_stride, int64_t row_stride, int V,
+                   const int32_t *tokens, const int32_t *cand_idx, const float *q,
+                   const int32_t *slot, const float *temperature, uint64_t seed, uint64_t step,
+                   int B, int N, int32_t *n_accept, int32_t *out_tokens, int32_t *status,
+                   void *ws, size_t ws_bytes, hipStream_t stream);
+size_t dflash2_verify_workspace_bytes(int B, int N, int V, int dtype);
+
+/* A short English description of a return code or of one status bit. */
+const char *dflash2_status_string(int code);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int dflash2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFLASH2_H */
