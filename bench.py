@@ -1,0 +1,285 @@
+#!/usr/bin/env python3
+"""Draft+verify steps/s of the DFlash2 step on one MI355X.
+
+One step is the whole hot path over one batch: per drafter layer the block attention and
+its four dynamic-conv sites, then top-16 over the draft rows, the selector and the verify
+(5 attention + 20 conv + 1 top-16 + 1 select + 1 verify calls of libdflash2). Inputs are
+seeded synthetic tensors already resident in HBM; several input sets are rotated so that
+the working set exceeds the 256 MiB last-level cache. Each step is one HIP-graph replay.
+
+Prints one JSON line: throughput, a roofline record for the block-attention call (its
+algorithmic bytes over its average duration, measured with HIP events on its stream) and
+the CPU oracle timed on a bounded sample on one host core.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
+LLC_BYTES = 256 << 20           # last-level (MALL) cache
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def attn_bytes_flops(cfg, ctx_len):
+    """Algorithmic bytes and FLOPs of one block-attention call: every visible context key
+    and value of each (sequence, KV head) read once, the queries and block keys/values read
+    once, the output written once; 4 * D FLOPs per (query row, visible key) pair."""
+    esz = 2 if cfg.act_bf16 else 4
+    per_key = cfg.Hkv * cfg.D * 2 * esz
+    fixed = (2 * cfg.P * cfg.Hq * cfg.D + 2 * cfg.P * cfg.Hkv * cfg.D) * esz
+    nbytes, flops = 0, 0
+    for L in ctx_len:
+        L = max(int(L), 0)
+        nbytes += min(L, cfg.W - 1) * per_key + fixed
+        for i in range(cfg.P):
+            keys = min(L, max(0, cfg.W - 1 - i)) + cfg.P
+            flops += 4 * cfg.D * cfg.Hq * keys
+    return nbytes, flops
+
+
+def set_bytes(cfg):
+    esz = 2 if cfg.act_bf16 else 4
+    ring = cfg.layers * 2 * cfg.B * cfg.S * cfg.Hkv * cfg.D * esz
+    logits = cfg.B * cfg.P * cfg.V * (esz + (4 if cfg.target_kind == "probs" else esz))
+    conv = cfg.sites * cfg.B * cfg.P * cfg.C * esz
+    return ring + logits + conv
+
+
+def traffic_record(workload):
+    """HBM bytes per attention launch from the committed PMC summary, if it was taken on
+    the current kernel source."""
+    path = os.path.join(PROFILES, "block_attn_counters.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, "block_drafter_draft_amd", "csrc", "block_attn.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if rec.get("source_sha256") != sha or rec.get("workload") != workload:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, seconds):
+    """The oracle, as it stands, on one host core: whole steps of the same workload, one
+    sequence at a time, for about `seconds`; scaled to steps/s of the full batch."""
+    import numpy as np
+
+    import oracle as orc
+    from block_drafter_draft_amd import workloads as wl
+    si = wl.make_step_inputs(cfg, iset=0)
+    B, P, N, V = cfg.B, cfg.P, cfg.N, cfg.V
+    t0 = time.perf_counter()
+    seqs_done = 0
+    while True:
+        b = seqs_done % B
+        sl = slice(b, b + 1)
+        for layer in range(cfg.layers):
+            orc.block_attn(*(np.ascontiguousarray(a[layer][sl]) for a in
+                             (si.q, si.k_blk, si.v_blk, si.k_ring, si.v_ring)),
+                           si.ctx_len[sl], cfg.W)
+        for s in range(cfg.sites):
+            orc.dynconv2(np.ascontiguousarray(si.conv_x[s][sl]), si.conv_base[s],
+                         np.ascontiguousarray(si.conv_delta[s][sl]))
+        ci, cv = orc.topk16(np.ascontiguousarray(si.draft[sl]).reshape(-1), 1, N, 1, P * V, V, V)
+        tok, slot, q, st = orc.select(ci, cv, np.ascontiguousarray(si.gate[sl]), si.pred_cb,
+                                      si.succ_cb, si.anchor[sl], si.temperature[sl], cfg.seed, 0)
+        orc.verify(np.ascontiguousarray(si.target[sl]).reshape(-1), 1, N, P * V, V, V, tok, ci, q,
+                   slot, si.temperature[sl], cfg.seed, 0, status=st)
+        seqs_done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds and seqs_done >= 1:
+            break
+    steps = seqs_done / B
+    return {"value": steps / el, "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{seqs_done} sequence(s) of full oracle steps ({steps:.3g} steps of batch "
+                      f"{B}) in {el:.1f} s on one host core"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5],
+                    help="input configuration (default: the drafter geometry at batch 1)")
+    ap.add_argument("--sets", type=int, default=0,
+                    help="input sets to rotate (default: enough to exceed the last-level cache)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a 1 GiB device copy (calibrates HBM byte counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the DFlash2 step shards by sequence with no "
+              "exchange, and this build has no multi-GPU path (--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from block_drafter_draft_amd import dflash2 as d2
+    from block_drafter_draft_amd import workloads as wl
+    from block_drafter_draft_amd.step import DeviceInputs, StepRunner
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    dev = "cuda:0"
+    cfg = wl.CONFIGS[args.workload]
+    nsets = args.sets or max(1, min(16, math.ceil(1.25 * LLC_BYTES / set_bytes(cfg))))
+    log(f"workload {cfg.cfg} ({cfg.name}), {nsets} input set(s) of {set_bytes(cfg) / 1e6:.1f} MB")
+    cb = wl.codebooks(cfg)
+    cb_dev = None
+    inputs = []
+    for i in range(nsets):
+        si = wl.make_step_inputs(cfg, iset=i, cb=cb)
+        di = DeviceInputs(si, dev, cb_dev)
+        cb_dev = (di.pred_cb, di.succ_cb)
+        inputs.append(di)
+        del si
+    runner = StepRunner(cfg, inputs, dev)
+    log("capturing graphs")
+    graphs = [runner.capture(i, step=i) for i in range(nsets)]
+    torch.cuda.synchronize()
+
+    for k in range(args.warmup):
+        graphs[k % nsets].replay()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for k in range(args.steps):
+        graphs[k % nsets].replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = ev0.elapsed_time(ev1)
+    ms_per_step = wall * 1e3 / args.steps
+
+    # steps with the host waiting for each step's tokens (a serving loop that must see them)
+    sync_steps = min(args.steps, 200)
+    host_out = torch.empty((cfg.B, cfg.N + 1), dtype=torch.int32, pin_memory=True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for k in range(sync_steps):
+        graphs[k % nsets].replay()
+        host_out.copy_(runner.out.out_tokens, non_blocking=True)
+        torch.cuda.synchronize()
+    ms_sync = (time.perf_counter() - t1) * 1e3 / sync_steps
+
+    # per-stage durations (eager calls bracketed by events on the library's stream)
+    def timed(fn, reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        tot = 0.0
+        for r in range(reps):
+            torch.cuda.synchronize()
+            a.record()
+            fn(r)
+            b.record()
+            torch.cuda.synchronize()
+            tot += a.elapsed_time(b)
+        return tot / reps
+
+    o = runner.out
+    B, P, N, V = cfg.B, cfg.P, cfg.N, cfg.V
+    reps = max(20, 4 * nsets)
+
+    def attn_call(r):
+        x = inputs[r % nsets]
+        layer = (r // nsets) % cfg.layers
+        d2.block_attn(x.q[layer], x.k_blk[layer], x.v_blk[layer], x.k_ring[layer],
+                      x.v_ring[layer], x.ctx_len, cfg.W, out=o.attn[layer], ws=runner.ws_attn)
+
+    def conv_call(r):
+        x = inputs[r % nsets]
+        s = (r // nsets) % cfg.sites
+        d2.dynconv2(x.conv_x[s], x.conv_base[s], x.conv_delta[s], out=o.conv[s])
+
+    def topk_call(r):
+        x = inputs[r % nsets]
+        d2.topk16(x.draft, B, N, 1, P * V, V, V, idx=o.cand_idx, val=o.cand_val, ws=runner.ws_topk)
+
+    def select_call(r):
+        x = inputs[r % nsets]
+        d2.select(o.cand_idx, o.cand_val, x.gate, x.pred_cb, x.succ_cb, x.anchor, x.temperature,
+                  cfg.seed, r, tokens=o.tokens, slot=o.slot, q=o.q, status=o.status,
+                  ws=runner.ws_sel)
+
+    def verify_call(r):
+        x = inputs[r % nsets]
+        d2.verify(x.target, B, N, P * V, V, V, o.tokens, o.cand_idx, o.q, o.slot, x.temperature,
+                  cfg.seed, r, o.status, n_accept=o.n_accept, out_tokens=o.out_tokens,
+                  ws=runner.ws_ver)
+
+    runner.run(0, 0)
+    stage_ms = {"block_attn": timed(attn_call, reps), "dynconv2": timed(conv_call, reps),
+                "topk16": timed(topk_call, reps), "select": timed(select_call, reps),
+                "verify": timed(verify_call, reps)}
+    attn_ms = stage_ms["block_attn"]
+    ctx = inputs[0].ctx_len.cpu().numpy()
+    a_bytes, a_flops = attn_bytes_flops(cfg, ctx)
+    achieved = a_bytes / (attn_ms * 1e-3) / 1e9
+    traffic = traffic_record(cfg.cfg)
+    mean_acc = float(o.n_accept.float().mean().item())
+
+    if args.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    result = {
+        "metric": "draft+verify steps/s at batch B (vocab 248320)",
+        "value": args.steps / wall,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.act_bf16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": B, "block": P, "vocab": V, "q_heads": cfg.Hq,
+                   "kv_heads": cfg.Hkv, "head_dim": cfg.D, "window": cfg.W, "width": cfg.C,
+                   "selector_rank": cfg.R, "layers": cfg.layers, "conv_sites": cfg.sites,
+                   "input_sets": nsets},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "dflash2_block_attn (split + combine)",
+                     "bytes_per_launch": a_bytes, "avg_launch_us": attn_ms * 1e3,
+                     "mfma_tflops": a_flops / (attn_ms * 1e-3) / 1e12,
+                     "mfma_frac": a_flops / (attn_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+        "stage_us": {k: v * 1e3 for k, v in stage_ms.items()},
+        "step_event_ms": ev_ms / args.steps,
+        "ms_per_step_host_sync": ms_sync,
+        "mean_accepted": mean_acc,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
