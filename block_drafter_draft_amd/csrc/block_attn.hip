@@ -5,14 +5,20 @@
 //
 // bf16 path (MFMA). The P block positions times the G = Hq/Hkv query heads of one KV head
 // form one 32-row query tile (8 x 4 = 32 at the drafter geometry), so the context ring of
-// each (sequence, KV head) is streamed once for all of them. One wave owns one split of
-// that ring: for each tile of 32 keys it computes S^T = K Q^T with
-// v_mfma_f32_32x32x16_bf16 (keys as rows, queries as columns), so each lane holds the
-// scores of a single query and the online softmax (max, rescale, sum) stays in-lane apart
-// from one exchange with the partner half-wave. The probabilities are then used directly
-// as the B operand of O^T = V^T P^T: the key order inside the contraction is permuted
-// to match the accumulator layout, and V is read through LDS in that same order. Splits
-// write unnormalised partial outputs with their (max, sum); a second kernel combines them.
+// each (sequence, KV head) is streamed from HBM once for all of them. A workgroup of four
+// waves owns one split of that ring and walks it in stages of 64 keys: the 256 threads
+// load a stage's K and V rows with 16-byte coalesced loads into padded LDS tiles, and the
+// next stage's loads are issued before the current stage is computed, so one stage (32 KiB)
+// is always in flight. Wave w takes 32-key tile (w & 1) of the stage and half (w >> 1) of
+// the head dimension: it computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys as rows,
+// queries as columns, so each lane owns one query's scores and the online softmax stays
+// in-lane apart from one exchange with the other half-wave), then uses its probabilities
+// directly as the B operand of O^T = V^T P^T for its 64 output columns; the key order in
+// that contraction is permuted to match the accumulator layout and V is read from LDS in
+// the same order (wave w covers columns [(w >> 1) D/2, (w >> 1 + 1) D/2)). At the end the
+// two tiles' states are merged through LDS. With one split
+// the workgroup writes the bf16 output; with several it writes an unnormalised partial and
+// its (max, sum), and a second kernel combines the splits.
 // Context position j of sequence b is in ring row j mod S; slot i sees positions j with
 // L_b + i - j < W, plus all P block keys.
 //
@@ -25,8 +31,23 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kRows = 32;       // query rows per tile
-constexpr int kKeys = 32;       // keys per tile
+constexpr int kRows = 32;    // query rows per tile
+constexpr int kStage = 64;   // keys per stage (two 32-key tiles)
+
+// Split planning: aim for kAttnTargetWGs workgroups, with at least kAttnMinStages stages
+// per split; stages in flight per workgroup: kAttnPrefetch (1 or 2).
+#ifndef DF2_ATTN_TARGET_WGS
+#define DF2_ATTN_TARGET_WGS 512
+#endif
+#ifndef DF2_ATTN_MIN_STAGES
+#define DF2_ATTN_MIN_STAGES 2
+#endif
+#ifndef DF2_ATTN_PREFETCH
+#define DF2_ATTN_PREFETCH 1
+#endif
+constexpr int kAttnTargetWGs = DF2_ATTN_TARGET_WGS;
+constexpr int kAttnMinStages = DF2_ATTN_MIN_STAGES;
+constexpr int kAttnPrefetch = DF2_ATTN_PREFETCH;
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ u32x4_t ld16(const uint16_t* p) {
@@ -34,103 +55,123 @@ __device__ __forceinline__ u32x4_t ld16(const uint16_t* p) {
 }
 
 template <int D>
-struct AttnSmem {
-  static constexpr int kVRS = D + 32;  // padded LDS row stride (elements)
-  uint16_t v[kKeys * kVRS];
+struct AttnShape {
+  static constexpr int KRS = D + 8;               // LDS row stride of K (elements)
+  static constexpr int VRS = D + 16;              // LDS row stride of V
+  static constexpr int VPR = D / 8;               // 16-byte vectors per key row
+  static constexpr int LOADS = kStage * VPR / 256;  // vectors per thread per tensor per stage
+  static constexpr int KS = D / 16;               // k-steps of QK^T
+  static constexpr int DTH = D / 64;              // 32-wide d tiles per half of D
 };
 
-// Split of the keys of one (sequence, KV head): context tiles [t0, t1), plus the block
-// keys in split 0.
 template <int D>
-__global__ __launch_bounds__(64) void attn_split_kernel(
+struct AttnSmem {
+  union {
+    struct {
+      uint16_t k[kStage * AttnShape<D>::KRS];
+      uint16_t v[kStage * AttnShape<D>::VRS];
+    } kv;
+    struct {
+      float o[2][AttnShape<D>::DTH][16][64];  // partner wave's O^T accumulators
+      float m[2][32], l[2][32];
+    } x;
+  };
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kb,
     const uint16_t* __restrict__ vb, const uint16_t* __restrict__ kr,
     const uint16_t* __restrict__ vr, const int32_t* __restrict__ ctx_len, int P, int Hq, int Hkv,
-    int S, int W, float scale_log2, int nsplit, float* __restrict__ ws_o,
-    float2* __restrict__ ws_ml) {
-  constexpr int KS = D / 16;  // k-steps of QK^T
-  constexpr int DT = D / 32;  // 32-wide d tiles of PV
-  constexpr int VRS = AttnSmem<D>::kVRS;
+    int S, int W, float scale_log2, int nsplit, int stages_per_split, float* __restrict__ ws_o,
+    float2* __restrict__ ws_ml, uint16_t* __restrict__ out) {
+  using SH = AttnShape<D>;
   __shared__ AttnSmem<D> sm;
-
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x, n = lane & 31, hh = lane >> 5;
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63, n = lane & 31, hh = lane >> 5;
+  const int tt = w & 1, dh = w >> 1;
   const int G = Hq / Hkv, rows = P * G;
   int L = ctx_len[b];
   L = L < 0 ? 0 : L;
   const int lo = L - W + 1 > 0 ? L - W + 1 : 0;  // oldest position any slot can see
-  const int nt = (L - lo + kKeys - 1) / kKeys;
-  const int tps = (nt + nsplit - 1) / nsplit;
-  const int t0 = split * tps;
-  const int t1 = nt < t0 + tps ? nt : t0 + tps;
+  const int c0 = split * stages_per_split * kStage + lo;   // first context key of the split
+  int c1 = c0 + stages_per_split * kStage;
+  c1 = c1 < L ? c1 : L;
+  const int nctx_st = c1 > c0 ? (c1 - c0 + kStage - 1) / kStage : 0;
+  // split 0 also takes the block keys, as its first stage (its loads go out with the rest)
+  const int blk_st = split == 0 ? 1 : 0;
+  const int nst = nctx_st + blk_st;
 
   // Q^T as the B operand: lane (n, hh) holds q[n][16 ks + 8 hh .. +7]
   const bool qvalid = n < rows;
   const int slot_n = qvalid ? n / G : 0;
   const int head_n = g * G + (qvalid ? n % G : 0);
   const uint16_t* qrow = q + (((int64_t)b * P + slot_n) * Hq + head_n) * D;
-  bf16x8_t qop[KS];
+  bf16x8_t qop[SH::KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    u32x4_t w = qvalid ? ld16(qrow + 16 * ks + 8 * hh) : u32x4_t{0, 0, 0, 0};
-    qop[ks] = __builtin_bit_cast(bf16x8_t, w);
+  for (int ks = 0; ks < SH::KS; ++ks) {
+    u32x4_t v = qvalid ? ld16(qrow + 16 * ks + 8 * hh) : u32x4_t{0, 0, 0, 0};
+    qop[ks] = __builtin_bit_cast(bf16x8_t, v);
   }
   const int jmin = L + slot_n - W + 1;  // this query's oldest visible position
 
-  float m = -INFINITY, l = 0.0f;
-  f32x16_t o[DT];
+  // Stage loads: vector vi = t + 256 u covers stage key vi / VPR, columns (vi % VPR) * 8.
+  // The thread's stage keys are kk0 + 256/VPR * u; their ring rows are found from one
+  // modulo per stage.
+  constexpr int KSTEP = 256 / SH::VPR;  // stage-key stride between a thread's vectors
+  const int kk0 = t / SH::VPR, d0 = (t % SH::VPR) * 8;
+  const int64_t head_off = (int64_t)g * D + d0;
+  auto load_stage = [&](int st, u32x4_t (&kreg)[SH::LOADS], u32x4_t (&vreg)[SH::LOADS]) {
+    if (st < blk_st) {
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16_t{};
-
-  const int ntiles = (t1 > t0 ? t1 - t0 : 0) + (split == 0 ? 1 : 0);
-  for (int it = 0; it < ntiles; ++it) {
-    const bool blk = it == ntiles - 1 && split == 0;
-    const int jbase = lo + (t0 + it) * kKeys;  // context tiles only
-    // key row addressing: the row held by lane (as A operand of QK) and V staging rows
-    auto key_ptr = [&](const uint16_t* ring, const uint16_t* block, int key, bool& valid) {
-      if (blk) {
-        valid = key < P;
-        return block + (((int64_t)b * P + (valid ? key : 0)) * Hkv + g) * D;
+      for (int u = 0; u < SH::LOADS; ++u) {
+        const int kk = kk0 + KSTEP * u;
+        const bool ok = kk < P;
+        const int64_t row = ((int64_t)b * P + (ok ? kk : 0)) * Hkv * D + head_off;
+        kreg[u] = ok ? ld16(kb + row) : u32x4_t{0, 0, 0, 0};
+        vreg[u] = ok ? ld16(vb + row) : u32x4_t{0, 0, 0, 0};
       }
-      const int j = jbase + key;
-      valid = j < L;
-      return ring + (((int64_t)b * S + (valid ? j % S : 0)) * Hkv + g) * D;
-    };
-    // K as the A operand: lane (key n, hh) holds k[key][16 ks + 8 hh .. +7]
-    bool kvalid;
-    const uint16_t* krow = key_ptr(kr, kb, n, kvalid);
-    u32x4_t ka[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) ka[ks] = kvalid ? ld16(krow + 16 * ks + 8 * hh) : u32x4_t{0, 0, 0, 0};
-    // V tile, coalesced: vector vi = v * 64 + lane covers key vi / (D/8), d (vi % (D/8)) * 8
-    constexpr int VPL = D / 16;  // vectors per lane
-    u32x4_t vv[VPL];
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      const int vi = v * 64 + lane;
-      const int key = vi / (D / 8), d0 = (vi % (D / 8)) * 8;
-      bool ok;
-      const uint16_t* vrow = key_ptr(vr, vb, key, ok);
-      vv[v] = ok ? ld16(vrow + d0) : u32x4_t{0, 0, 0, 0};
+      return;
     }
-
-    f32x16_t s = f32x16_t{};
+    const int j0 = c0 + (st - blk_st) * kStage + kk0;
+    int jm = j0 % S;
+    const int kstep_mod = KSTEP % S;  // < S, so one wrap check keeps jm in [0, S)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka[ks]), qop[ks], s, 0, 0, 0);
+    for (int u = 0; u < SH::LOADS; ++u) {
+      const bool ok = j0 + KSTEP * u < c1;
+      const int64_t row = ((int64_t)b * S + (ok ? jm : 0)) * Hkv * D + head_off;
+      kreg[u] = ok ? ld16(kr + row) : u32x4_t{0, 0, 0, 0};
+      vreg[u] = ok ? ld16(vr + row) : u32x4_t{0, 0, 0, 0};
+      jm += kstep_mod;
+      jm = jm >= S ? jm - S : jm;
+    }
+  };
 
-    // scores: accumulator i of lane (n, hh) is key 8(i/4) + 4hh + i%4 of this tile
+  float m = -INFINITY, l = 0.0f;
+  f32x16_t o[SH::DTH];
+#pragma unroll
+  for (int i = 0; i < SH::DTH; ++i) o[i] = f32x16_t{};
+
+  auto compute_stage = [&](int st) {
+    const bool blk = st < blk_st;
+    const int jb = c0 + (st - blk_st) * kStage;
+    // S^T for tile tt: accumulator i of lane (n, hh) is key 32 tt + 8(i/4) + 4hh + i%4
+    f32x16_t s = f32x16_t{};
+    const uint16_t* krow = &sm.kv.k[(32 * tt + n) * SH::KRS + 8 * hh];
+#pragma unroll
+    for (int ks = 0; ks < SH::KS; ++ks)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(krow + 16 * ks)), qop[ks], s,
+          0, 0, 0);
+    // visible keys of this tile: a block stage keeps keys [0, P); a context stage keeps
+    // positions j in [max(jb, jmin), c1), i.e. tile keys [klo, khi)
+    const int klo = blk ? 0 : (jmin > jb ? jmin - jb : 0);
+    const int khi = blk ? P : c1 - jb;
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int key = 8 * (i >> 2) + 4 * hh + (i & 3);
-      bool vis;
-      if (blk) {
-        vis = key < P;
-      } else {
-        const int j = jbase + key;
-        vis = j < L && j >= jmin;
-      }
+      const int kk = 32 * tt + 8 * (i >> 2) + 4 * hh + (i & 3);
+      const bool vis = kk >= klo && kk < khi;
       s[i] = vis ? s[i] * scale_log2 : -INFINITY;
       mx = fmaxf(mx, s[i]);
     }
@@ -148,100 +189,201 @@ __global__ __launch_bounds__(64) void attn_split_kernel(
     l = l * alpha + psum;
     m = mnew;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-
-    // stage V (row = key) in LDS
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      const int vi = v * 64 + lane;
-      const int key = vi / (D / 8), d0 = (vi % (D / 8)) * 8;
-      *reinterpret_cast<u32x4_t*>(&sm.v[key * VRS + d0]) = vv[v];
-    }
-    __syncthreads();
-
-    // P^T as the B operand, k-step t: lane's own accumulators 8t .. 8t+7, i.e. keys
-    // 16t + 8(e/4) + 4hh + e%4 for element e
+    for (int i = 0; i < SH::DTH; ++i) o[i] *= alpha;
+    // P^T as the B operand, k-step u: own accumulators 8u .. 8u+7 = keys 16u + 8(e/4) + 4hh + e%4
     bf16x8_t pb[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pb[t][e] = (__bf16)s[8 * t + e];
-    }
+      for (int e = 0; e < 8; ++e) pb[u][e] = (__bf16)s[8 * u + e];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int d = 32 * dt + n;
+    for (int i = 0; i < SH::DTH; ++i) {
+      const int d = (D / 2) * dh + 32 * i + n;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int u = 0; u < 2; ++u) {
         bf16x8_t va;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int key = 16 * t + 8 * (e >> 2) + 4 * hh + (e & 3);
-          va[e] = __builtin_bit_cast(__bf16, sm.v[key * VRS + d]);
+          const int kk = 32 * tt + 16 * u + 8 * (e >> 2) + 4 * hh + (e & 3);
+          va[e] = __builtin_bit_cast(__bf16, sm.kv.v[kk * SH::VRS + d]);
         }
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[t], o[dt], 0, 0, 0);
+        o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[u], o[i], 0, 0, 0);
       }
     }
-    __syncthreads();
+  };
+  auto store_stage = [&](const u32x4_t (&kreg)[SH::LOADS], const u32x4_t (&vreg)[SH::LOADS]) {
+#pragma unroll
+    for (int u = 0; u < SH::LOADS; ++u) {
+      const int kk = kk0 + KSTEP * u;
+      *reinterpret_cast<u32x4_t*>(&sm.kv.k[kk * SH::KRS + d0]) = kreg[u];
+      *reinterpret_cast<u32x4_t*>(&sm.kv.v[kk * SH::VRS + d0]) = vreg[u];
+    }
+  };
+
+  if constexpr (kAttnPrefetch == 2) {
+    // two stages in flight: registers A hold even stages, B odd ones
+    u32x4_t ka[SH::LOADS], va_[SH::LOADS], kb2[SH::LOADS], vb2[SH::LOADS];
+    if (nst > 0) load_stage(0, ka, va_);
+    if (nst > 1) load_stage(1, kb2, vb2);
+    for (int st = 0; st < nst; st += 2) {
+      store_stage(ka, va_);
+      __syncthreads();
+      if (st + 2 < nst) load_stage(st + 2, ka, va_);
+      compute_stage(st);
+      __syncthreads();
+      if (st + 1 >= nst) break;
+      store_stage(kb2, vb2);
+      __syncthreads();
+      if (st + 3 < nst) load_stage(st + 3, kb2, vb2);
+      compute_stage(st + 1);
+      __syncthreads();
+    }
+  } else {
+    // one stage in flight
+    u32x4_t ka[SH::LOADS], va_[SH::LOADS];
+    if (nst > 0) load_stage(0, ka, va_);
+    for (int st = 0; st < nst; ++st) {
+      store_stage(ka, va_);
+      __syncthreads();
+      if (st + 1 < nst) load_stage(st + 1, ka, va_);
+      compute_stage(st);
+      __syncthreads();
+    }
   }
 
-  // partial result: O^T accumulator i of d tile dt is d = 32dt + 8(i/4) + 4hh + i%4
+  // merge tile 1 into tile 0 (same d half): waves 1 and 3 hand their state to 0 and 2
+  if (tt == 1) {
+#pragma unroll
+    for (int i = 0; i < SH::DTH; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sm.x.o[dh][i][r][lane] = o[i][r];
+    if (hh == 0) {
+      sm.x.m[dh][n] = m;
+      sm.x.l[dh][n] = l;
+    }
+  }
+  __syncthreads();
+  if (tt == 1) return;
+  {
+    const float m1 = sm.x.m[dh][n], l1 = sm.x.l[dh][n];
+    const float M = fmaxf(m, m1);
+    const float a0 = M == -INFINITY ? 0.0f : exp2f(m - M);
+    const float a1 = M == -INFINITY ? 0.0f : exp2f(m1 - M);
+    l = l * a0 + l1 * a1;
+    m = M;
+#pragma unroll
+    for (int i = 0; i < SH::DTH; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[i][r] = o[i][r] * a0 + sm.x.o[dh][i][r][lane] * a1;
+  }
+  // accumulator r of d tile i is column d = (D/2) dh + 32 i + 8(r/4) + 4hh + r%4
+  if (nsplit == 1) {
+    if (!qvalid) return;
+    const float inv = 1.0f / l;
+    uint16_t* dst = out + (((int64_t)b * P + slot_n) * Hq + head_n) * D;
+#pragma unroll
+    for (int i = 0; i < SH::DTH; ++i)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int d = (D / 2) * dh + 32 * i + 8 * a + 4 * hh;
+        const uint32_t lo2 = (uint32_t)f32_to_bf16(o[i][4 * a] * inv) |
+                             ((uint32_t)f32_to_bf16(o[i][4 * a + 1] * inv) << 16);
+        const uint32_t hi2 = (uint32_t)f32_to_bf16(o[i][4 * a + 2] * inv) |
+                             ((uint32_t)f32_to_bf16(o[i][4 * a + 3] * inv) << 16);
+        *reinterpret_cast<uint2*>(dst + d) = make_uint2(lo2, hi2);
+      }
+    return;
+  }
   const int64_t part = ((int64_t)b * Hkv + g) * nsplit + split;
   float* po = ws_o + (part * kRows + n) * D;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+  for (int i = 0; i < SH::DTH; ++i)
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      const int d = 32 * dt + 8 * a + 4 * hh;
+      const int d = (D / 2) * dh + 32 * i + 8 * a + 4 * hh;
       *reinterpret_cast<float4*>(po + d) =
-          make_float4(o[dt][4 * a + 0], o[dt][4 * a + 1], o[dt][4 * a + 2], o[dt][4 * a + 3]);
+          make_float4(o[i][4 * a], o[i][4 * a + 1], o[i][4 * a + 2], o[i][4 * a + 3]);
     }
-  if (hh == 0) ws_ml[part * kRows + n] = make_float2(m, l);
+  if (dh == 0 && hh == 0) ws_ml[part * kRows + n] = make_float2(m, l);
 }
 
-template <int D>
+// Combines the splits of one (sequence, KV head, quarter of D). The (max, sum) pairs of all
+// splits are read in one parallel batch into LDS and turned into weights; then thread (n, c)
+// (query row n, 4 consecutive columns) issues the loads of all its split partials before
+// using any of them.
+constexpr int kMaxSplits = 32;
+
+template <int D, int MS>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ ws_o,
                                                            const float2* __restrict__ ws_ml, int P,
                                                            int Hq, int Hkv, int nsplit,
                                                            uint16_t* __restrict__ out) {
-  const int g = blockIdx.x, b = blockIdx.y;
-  const int n = threadIdx.x >> 3, part = threadIdx.x & 7;
-  const int G = Hq / Hkv;
-  if (n >= P * G) return;
-  constexpr int DPT = D / 8;
+  __shared__ float wgt[MS][kRows], lsum[MS][kRows];
+  __shared__ float inv_den[kRows];
+  const int g = blockIdx.x, b = blockIdx.y, quarter = blockIdx.z;
+  const int t = threadIdx.x;
+  const int G = Hq / Hkv, rows = P * G;
   const int64_t p0 = ((int64_t)b * Hkv + g) * nsplit;
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ws_ml[(p0 + s) * kRows + n].x);
-  float acc[DPT];
+  for (int e = t; e < MS * kRows; e += 256) {
+    const int s = e / kRows;
+    const float2 ml = s < nsplit ? ws_ml[p0 * kRows + e] : make_float2(-INFINITY, 0.0f);
+    wgt[s][e % kRows] = ml.x;
+    lsum[s][e % kRows] = ml.y;
+  }
+  __syncthreads();
+  if (t < kRows) {
+    float M = -INFINITY;
 #pragma unroll
-  for (int e = 0; e < DPT; ++e) acc[e] = 0.0f;
-  float den = 0.0f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float2 ml = ws_ml[(p0 + s) * kRows + n];
-    if (ml.x == -INFINITY) continue;
-    const float w = exp2f(ml.x - M);
-    den += w * ml.y;
-    const float* po = ws_o + ((p0 + s) * kRows + n) * D + part * DPT;
+    for (int s = 0; s < MS; ++s) M = fmaxf(M, wgt[s][t]);
+    float den = 0.0f;
 #pragma unroll
-    for (int e = 0; e < DPT; e += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(po + e);
-      acc[e] += w * v.x;
-      acc[e + 1] += w * v.y;
-      acc[e + 2] += w * v.z;
-      acc[e + 3] += w * v.w;
+    for (int s = 0; s < MS; ++s) {
+      const float ms = wgt[s][t];
+      const float w = ms == -INFINITY ? 0.0f : exp2f(ms - M);
+      den += w * lsum[s][t];
+      wgt[s][t] = w;  // splits past nsplit (and empty ones) weigh 0
     }
+    inv_den[t] = 1.0f / den;
   }
-  const float inv = 1.0f / den;
+  __syncthreads();
+  const int n = t >> 3, c = t & 7;
+  if (n >= rows || c * 4 >= D / 4) return;  // D/16 threads cover a row's quarter
+  const int d = quarter * (D / 4) + c * 4;
+  float4 v[MS];
+#pragma unroll
+  for (int s = 0; s < MS; ++s) {
+    const int sc = s < nsplit ? s : nsplit - 1;  // in range, so the loads carry no conditions
+    v[s] = *reinterpret_cast<const float4*>(ws_o + ((p0 + sc) * kRows + n) * D + d);
+  }
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int s = 0; s < MS; ++s) {
+    const float w = wgt[s][n];
+    acc.x += w * v[s].x;
+    acc.y += w * v[s].y;
+    acc.z += w * v[s].z;
+    acc.w += w * v[s].w;
+  }
+  const float inv = inv_den[n];
   const int slot = n / G, head = g * G + n % G;
-  uint16_t* dst = out + (((int64_t)b * P + slot) * Hq + head) * D + part * DPT;
-#pragma unroll
-  for (int e = 0; e < DPT; e += 8) {
-    uint32_t w4[4];
-#pragma unroll
-    for (int h = 0; h < 4; ++h)
-      w4[h] = (uint32_t)f32_to_bf16(acc[e + 2 * h] * inv) |
-              ((uint32_t)f32_to_bf16(acc[e + 2 * h + 1] * inv) << 16);
-    *reinterpret_cast<uint4*>(dst + e) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-  }
+  uint16_t* dst = out + (((int64_t)b * P + slot) * Hq + head) * D + d;
+  const uint32_t lo2 = (uint32_t)f32_to_bf16(acc.x * inv) | ((uint32_t)f32_to_bf16(acc.y * inv) << 16);
+  const uint32_t hi2 = (uint32_t)f32_to_bf16(acc.z * inv) | ((uint32_t)f32_to_bf16(acc.w * inv) << 16);
+  *reinterpret_cast<uint2*>(dst) = make_uint2(lo2, hi2);
+}
+
+template <int D>
+void launch_combine(const float* ws_o, const float2* ws_ml, int B, int P, int Hq, int Hkv, int nsplit,
+                    uint16_t* out, hipStream_t stream) {
+  const dim3 grid(Hkv, B, 4);
+  if (nsplit <= 4)
+    attn_combine_kernel<D, 4><<<grid, 256, 0, stream>>>(ws_o, ws_ml, P, Hq, Hkv, nsplit, out);
+  else if (nsplit <= 8)
+    attn_combine_kernel<D, 8><<<grid, 256, 0, stream>>>(ws_o, ws_ml, P, Hq, Hkv, nsplit, out);
+  else if (nsplit <= 16)
+    attn_combine_kernel<D, 16><<<grid, 256, 0, stream>>>(ws_o, ws_ml, P, Hq, Hkv, nsplit, out);
+  else
+    attn_combine_kernel<D, 32><<<grid, 256, 0, stream>>>(ws_o, ws_ml, P, Hq, Hkv, nsplit, out);
 }
 
 // f32: one wave per query row; lanes hold d and d + 64.
@@ -290,12 +432,26 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(
   }
 }
 
-int plan_splits(int B, int Hkv, int W) {
-  const int max_tiles = (W - 1 + kKeys - 1) / kKeys;
-  int by_size = (max_tiles + 1) / 2;  // at least ~2 tiles per split
-  int by_grid = (2048 + B * Hkv - 1) / (B * Hkv);
-  int s = by_size < by_grid ? by_size : by_grid;
-  return s < 1 ? 1 : s;
+struct SplitPlan {
+  int nsplit;
+  int stages_per_split;
+};
+
+// Enough workgroups to cover the chip at small batch, one split per (sequence, KV head)
+// once the batch alone does.
+SplitPlan plan_splits(int B, int Hkv, int W) {
+  const int stages = (W - 1 + kStage - 1) / kStage;  // stages of the widest window
+  const int want = (kAttnTargetWGs + B * Hkv - 1) / (B * Hkv);
+  int cap = stages / kAttnMinStages > 1 ? stages / kAttnMinStages : 1;
+  cap = cap < kMaxSplits ? cap : kMaxSplits;
+  int ns = want < cap ? want : cap;
+  ns = ns < 1 ? 1 : ns;
+  SplitPlan p;
+  p.stages_per_split = (stages + ns - 1) / ns;
+  p.stages_per_split = p.stages_per_split < 1 ? 1 : p.stages_per_split;
+  p.nsplit = (stages + p.stages_per_split - 1) / p.stages_per_split;
+  p.nsplit = p.nsplit < 1 ? 1 : p.nsplit;
+  return p;
 }
 
 }  // namespace
@@ -310,8 +466,9 @@ extern "C" size_t dflash2_block_attn_workspace_bytes(int B, int P, int Hq, int H
   (void)S;
   if (B < 1 || Hkv < 1 || W < 1 || (D != 64 && D != 128)) return 0;
   if (dtype != DFLASH2_BF16) return 0;
-  const int ns = plan_splits(B, Hkv, W);
-  const size_t parts = (size_t)B * Hkv * ns;
+  const SplitPlan sp = plan_splits(B, Hkv, W);
+  if (sp.nsplit == 1) return 0;
+  const size_t parts = (size_t)B * Hkv * sp.nsplit;
   return round_up(parts * kRows * D * sizeof(float), kWsAlign) +
          round_up(parts * kRows * sizeof(float2), kWsAlign);
 }
@@ -340,27 +497,26 @@ extern "C" int dflash2_block_attn(const void* q, const void* k_blk, const void* 
   for (const void* p : {q, k_blk, v_blk, k_ring, v_ring, (const void*)out})
     if (!aligned(p, 16)) return DFLASH2_EUNSUPPORTED;
   const size_t need = dflash2_block_attn_workspace_bytes(B, P, Hq, Hkv, D, S, W, dtype);
-  if (!ws || !aligned(ws, kWsAlign) || ws_bytes < need) return DFLASH2_EWORKSPACE;
-  const int ns = plan_splits(B, Hkv, W);
-  const size_t parts = (size_t)B * Hkv * ns;
-  float* ws_o = (float*)ws;
-  float2* ws_ml = (float2*)((char*)ws + round_up(parts * kRows * D * sizeof(float), kWsAlign));
+  if (need && (!ws || !aligned(ws, kWsAlign) || ws_bytes < need)) return DFLASH2_EWORKSPACE;
+  const SplitPlan sp = plan_splits(B, Hkv, W);
+  const size_t parts = (size_t)B * Hkv * sp.nsplit;
+  float* ws_o = need ? (float*)ws : nullptr;
+  float2* ws_ml =
+      need ? (float2*)((char*)ws + round_up(parts * kRows * D * sizeof(float), kWsAlign)) : nullptr;
   const float sl2 = scale * kLog2e;
-  dim3 grid(ns, Hkv, B);
+  dim3 grid(sp.nsplit, Hkv, B);
   if (D == 128) {
-    attn_split_kernel<128><<<grid, 64, 0, stream>>>(
+    attn_split_kernel<128><<<grid, 256, 0, stream>>>(
         (const uint16_t*)q, (const uint16_t*)k_blk, (const uint16_t*)v_blk,
-        (const uint16_t*)k_ring, (const uint16_t*)v_ring, ctx_len, P, Hq, Hkv, S, W, sl2, ns, ws_o,
-        ws_ml);
-    attn_combine_kernel<128><<<dim3(Hkv, B), 256, 0, stream>>>(ws_o, ws_ml, P, Hq, Hkv, ns,
-                                                               (uint16_t*)out);
+        (const uint16_t*)k_ring, (const uint16_t*)v_ring, ctx_len, P, Hq, Hkv, S, W, sl2,
+        sp.nsplit, sp.stages_per_split, ws_o, ws_ml, (uint16_t*)out);
+    if (sp.nsplit > 1) launch_combine<128>(ws_o, ws_ml, B, P, Hq, Hkv, sp.nsplit, (uint16_t*)out, stream);
   } else {
-    attn_split_kernel<64><<<grid, 64, 0, stream>>>(
+    attn_split_kernel<64><<<grid, 256, 0, stream>>>(
         (const uint16_t*)q, (const uint16_t*)k_blk, (const uint16_t*)v_blk,
-        (const uint16_t*)k_ring, (const uint16_t*)v_ring, ctx_len, P, Hq, Hkv, S, W, sl2, ns, ws_o,
-        ws_ml);
-    attn_combine_kernel<64><<<dim3(Hkv, B), 256, 0, stream>>>(ws_o, ws_ml, P, Hq, Hkv, ns,
-                                                              (uint16_t*)out);
+        (const uint16_t*)k_ring, (const uint16_t*)v_ring, ctx_len, P, Hq, Hkv, S, W, sl2,
+        sp.nsplit, sp.stages_per_split, ws_o, ws_ml, (uint16_t*)out);
+    if (sp.nsplit > 1) launch_combine<64>(ws_o, ws_ml, B, P, Hq, Hkv, sp.nsplit, (uint16_t*)out, stream);
   }
   return launch_status();
 }

@@ -238,7 +238,111 @@ __device__ __forceinline__ uint32_t wave_sort_desc_u32(uint32_t v) {
   return v;
 }
 
-// Block-wide inclusive/exclusive helpers use LDS scratch passed by the caller.
+// ---------------------------------------------------------------------------------------
+// Row chunks read by a 256-thread workgroup. With 16-byte loads (VEC), element e of thread
+// t sits at chunk offset (e / EPV) * 256 * EPV + t * EPV + e % EPV (each load instruction of
+// a wave covers 1 KiB contiguous); otherwise at e * 256 + t. Either way a thread visits its
+// elements in increasing index order. Elements at or past V read as 0.
+// ---------------------------------------------------------------------------------------
+
+constexpr int kChunkThreads = 256;
+
+template <class KT, int EPT>
+struct ChunkLoad {
+  using E = typename KT::elem_t;
+  static constexpr int kEPV = 16 / (int)sizeof(E);  // elements per 16-byte vector
+  static constexpr int kNV = EPT / kEPV;              // vectors per thread
+};
+
+// element e of thread t lives at chunk offset (e / EPV) * 256 * EPV + t * EPV + e % EPV
+template <int EPV>
+__device__ __forceinline__ int elem_offset(int t, int e) {
+  return (e / EPV) * (kChunkThreads * EPV) + t * EPV + (e % EPV);
+}
+
+template <class KT, int EPT, bool VEC>
+__device__ __forceinline__ void load_chunk(const typename KT::elem_t* __restrict__ row, int base,
+                                           int V, uint32_t (&bits)[EPT]) {
+  using E = typename KT::elem_t;
+  const int t = threadIdx.x;
+  if constexpr (VEC) {
+    constexpr int EPV = ChunkLoad<KT, EPT>::kEPV;
+#pragma unroll
+    for (int v = 0; v < EPT / EPV; ++v) {
+      int off = base + v * (kChunkThreads * EPV) + t * EPV;
+      if (off + EPV <= V) {
+        const u32x4_t w = *reinterpret_cast<const u32x4_t*>(row + off);
+        const uint32_t ws[4] = {w[0], w[1], w[2], w[3]};
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          if constexpr (sizeof(E) == 2)
+            bits[v * EPV + e] = (ws[e / 2] >> (16 * (e & 1))) & 0xffffu;
+          else
+            bits[v * EPV + e] = ws[e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          int x = off + e;
+          uint32_t u = 0;
+          if (x < V) {
+            if constexpr (sizeof(E) == 2)
+              u = reinterpret_cast<const uint16_t*>(row)[x];
+            else
+              u = __float_as_uint(reinterpret_cast<const float*>(row)[x]);
+          }
+          bits[v * EPV + e] = u;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      int x = base + e * kChunkThreads + t;
+      uint32_t u = 0;
+      if (x < V) {
+        if constexpr (sizeof(E) == 2)
+          u = reinterpret_cast<const uint16_t*>(row)[x];
+        else
+          u = __float_as_uint(reinterpret_cast<const float*>(row)[x]);
+      }
+      bits[e] = u;
+    }
+  }
+}
+
+// A chunk that lies wholly inside the row with 16-byte aligned rows: every load is issued
+// unconditionally before any is used, so a thread's loads are in flight together.
+template <class KT, int EPT>
+__device__ __forceinline__ void load_chunk_full(const typename KT::elem_t* __restrict__ row,
+                                                int base, uint32_t (&bits)[EPT]) {
+  using E = typename KT::elem_t;
+  constexpr int EPV = 16 / (int)sizeof(E);
+  constexpr int NV = EPT / EPV;
+  const int t = threadIdx.x;
+  u32x4_t w[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v)
+    w[v] = *reinterpret_cast<const u32x4_t*>(row + base + v * (kChunkThreads * EPV) + t * EPV);
+#pragma unroll
+  for (int v = 0; v < NV; ++v)
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+      if constexpr (sizeof(E) == 2)
+        bits[v * EPV + e] = (w[v][e / 2] >> (16 * (e & 1))) & 0xffffu;
+      else
+        bits[v * EPV + e] = w[v][e];
+    }
+}
+
+template <int EPT, bool VEC, class KT>
+__device__ __forceinline__ int index_of(int base, int e) {
+  if constexpr (VEC)
+    return base + elem_offset<ChunkLoad<KT, EPT>::kEPV>(threadIdx.x, e);
+  else
+    return base + e * kChunkThreads + threadIdx.x;
+}
+
 
 // ---------------------------------------------------------------------------------------
 // Host-side launch helper

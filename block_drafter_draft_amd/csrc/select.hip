@@ -19,6 +19,10 @@ namespace {
 constexpr int kMaxN = 15;
 constexpr int kMaxR = 512;
 
+// LDS row stride in elements: 8 extra bf16 keep rows 16-byte aligned and shift the banks
+__host__ __device__ inline int lat_row_stride(int R) { return ((R + 7) / 8) * 8 + 8; }
+
+template <bool VEC>
 __global__ __launch_bounds__(256) void select_lattice_kernel(
     const int32_t* __restrict__ cidx, const float* __restrict__ cval,
     const float* __restrict__ gate, const uint16_t* __restrict__ pred_cb,
@@ -29,10 +33,10 @@ __global__ __launch_bounds__(256) void select_lattice_kernel(
   const int b = blockIdx.y;
   const int t = threadIdx.x;
   const int kp = t >> 4, k = t & 15;
-  const int RS = R + 2;  // padded row stride in bf16 elements
-  uint16_t* A = reinterpret_cast<uint16_t*>(smem);          // [16][RS]
-  uint16_t* Bm = A + 16 * RS;                               // [16][RS]
-  float* g = reinterpret_cast<float*>(Bm + 16 * RS + 2);    // [R] (4-byte aligned)
+  const int RS = lat_row_stride(R);
+  uint16_t* A = reinterpret_cast<uint16_t*>(smem);  // [16][RS] predecessor rows
+  uint16_t* Bm = A + 16 * RS;                       // [16][RS] successor rows
+  float* g = reinterpret_cast<float*>(Bm + 16 * RS);  // [RS] gate (zero padded)
   __shared__ int32_t prow[kTopK], srow[kTopK];
 
   const int npred = i == 1 ? 1 : kTopK;
@@ -44,26 +48,75 @@ __global__ __launch_bounds__(256) void select_lattice_kernel(
   }
   __syncthreads();
   const float* gi = gate + ((int64_t)b * N + (i - 1)) * R;
-  for (int r = t; r < R; r += 256) g[r] = gi[r];
-  for (int e = t; e < npred * R; e += 256) {
-    const int row = e / R, r = e % R;
-    const int32_t p = prow[row];
-    A[row * RS + r] = p >= 0 ? pred_cb[(int64_t)p * R + r] : (uint16_t)0;
-  }
-  for (int e = t; e < kTopK * R; e += 256) {
-    const int row = e / R, r = e % R;
-    const int32_t c = srow[row];
-    Bm[row * RS + r] = c >= 0 ? succ_cb[(int64_t)c * R + r] : (uint16_t)0;
+  if constexpr (VEC) {
+    // R % 8 == 0: 16-byte row pieces; every load of the thread is issued before any store
+    const int vpr = R / 8;
+    const int nvec = (npred + kTopK) * vpr;
+    constexpr int kMaxPer = 2 * kTopK * (512 / 8) / 256;  // R <= 512
+    u32x4_t buf[kMaxPer];
+#pragma unroll
+    for (int u = 0; u < kMaxPer; ++u) {
+      const int e = t + 256 * u;
+      buf[u] = u32x4_t{0, 0, 0, 0};
+      if (e < nvec) {
+        const int row = e / vpr, c8 = (e % vpr) * 8;
+        const int32_t r = row < npred ? prow[row] : srow[row - npred];
+        const uint16_t* src = row < npred ? pred_cb : succ_cb;
+        if (r >= 0) buf[u] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)r * R + c8);
+      }
+    }
+    float4 gv = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (t < R / 4) gv = reinterpret_cast<const float4*>(gi)[t];
+#pragma unroll
+    for (int u = 0; u < kMaxPer; ++u) {
+      const int e = t + 256 * u;
+      if (e < nvec) {
+        const int row = e / vpr, c8 = (e % vpr) * 8;
+        uint16_t* dst = row < npred ? A + row * RS : Bm + (row - npred) * RS;
+        *reinterpret_cast<u32x4_t*>(dst + c8) = buf[u];
+      }
+    }
+    if (t < R / 4) reinterpret_cast<float4*>(g)[t] = gv;
+  } else {
+    for (int r = t; r < R; r += 256) g[r] = gi[r];
+    for (int e = t; e < npred * R; e += 256) {
+      const int row = e / R, r = e % R;
+      const int32_t p = prow[row];
+      A[row * RS + r] = p >= 0 ? pred_cb[(int64_t)p * R + r] : (uint16_t)0;
+    }
+    for (int e = t; e < kTopK * R; e += 256) {
+      const int row = e / R, r = e % R;
+      const int32_t c = srow[row];
+      Bm[row * RS + r] = c >= 0 ? succ_cb[(int64_t)c * R + r] : (uint16_t)0;
+    }
   }
   __syncthreads();
   if (kp >= npred) return;
   const uint16_t* a = A + kp * RS;
   const uint16_t* bb = Bm + k * RS;
   float acc = 0.0f;
-  for (int r = 0; r < R; ++r) {
-    const float ag = __fmul_rn(bf16_to_f32(a[r]), g[r]);
-    const float pr = __fmul_rn(ag, bf16_to_f32(bb[r]));
-    acc = __fadd_rn(acc, pr);
+  int r = 0;
+  if constexpr (VEC) {
+    // eight terms per LDS access, still added one at a time in order
+    for (; r < R; r += 8) {
+      const u32x4_t a8 = *reinterpret_cast<const u32x4_t*>(a + r);
+      const u32x4_t b8 = *reinterpret_cast<const u32x4_t*>(bb + r);
+      const float4 g0 = *reinterpret_cast<const float4*>(g + r);
+      const float4 g1 = *reinterpret_cast<const float4*>(g + r + 4);
+      const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float av = bf16_to_f32((a8[e / 2] >> (16 * (e & 1))) & 0xffffu);
+        const float bv = bf16_to_f32((b8[e / 2] >> (16 * (e & 1))) & 0xffffu);
+        acc = __fadd_rn(acc, __fmul_rn(__fmul_rn(av, gg[e]), bv));
+      }
+    }
+  } else {
+    for (; r < R; ++r) {
+      const float ag = __fmul_rn(bf16_to_f32(a[r]), g[r]);
+      const float pr = __fmul_rn(ag, bf16_to_f32(bb[r]));
+      acc = __fadd_rn(acc, pr);
+    }
   }
   const float v = cval[((int64_t)b * N + (i - 1)) * kTopK + k];
   lattice[(((int64_t)b * N + (i - 1)) * kTopK + kp) * kTopK + k] = __fadd_rn(v, acc);
@@ -96,14 +149,24 @@ __global__ __launch_bounds__(64) void select_path_kernel(
   // scores into LDS; every computed score and value must be finite
   int nonfin = 0;
   if (ok) {
-    for (int e = lane; e < N * kTopK * kTopK; e += 64) {
-      const int i = e / (kTopK * kTopK) + 1, kp = (e / kTopK) % kTopK, k = e % kTopK;
-      const float s = lattice[(int64_t)b * N * kTopK * kTopK + e];
-      S[i - 1][kp][k] = s;
-      if (i == 1 && kp > 0) continue;  // slot 1 has the anchor as its only predecessor
-      const float v = cval[((int64_t)b * N + (i - 1)) * kTopK + k];
-      nonfin |= !(fabsf(s) <= 3.40282347e38f) || !(fabsf(v) <= 3.40282347e38f);
+    // 4 scores per lane per step, several steps in flight
+    const float4* lat4 = reinterpret_cast<const float4*>(lattice + (int64_t)b * N * kTopK * kTopK);
+    float* Sf = &S[0][0][0];
+#pragma unroll 4
+    for (int e4 = lane; e4 < N * kTopK * kTopK / 4; e4 += 64) {
+      const float4 s4 = lat4[e4];
+      const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const int e = 4 * e4 + h;
+        const int i = e / (kTopK * kTopK) + 1, kp = (e / kTopK) % kTopK;
+        Sf[e] = sv[h];
+        // slot 1 has the anchor as its only predecessor (row 0)
+        if (!(i == 1 && kp > 0)) nonfin |= !(fabsf(sv[h]) <= 3.40282347e38f);
+      }
     }
+    for (int e = lane; e < N * kTopK; e += 64)
+      nonfin |= !(fabsf(cval[(int64_t)b * N * kTopK + e]) <= 3.40282347e38f);
   }
   const bool finite = wave_or(nonfin) == 0;
   if (ok && !finite) st |= DFLASH2_ST_NONFINITE;
@@ -219,9 +282,15 @@ extern "C" int dflash2_select(const int32_t* cand_idx, const float* cand_val, co
   if (!aligned(ws, kWsAlign) || ws_bytes < dflash2_select_workspace_bytes(B, N))
     return DFLASH2_EWORKSPACE;
   float* lattice = (float*)ws;
-  const size_t lds = (size_t)2 * kTopK * (R + 2) * sizeof(uint16_t) + 4 + (size_t)R * sizeof(float);
-  select_lattice_kernel<<<dim3(N, B), 256, lds, stream>>>(cand_idx, cand_val, gate, pred_cb, succ_cb,
-                                                         V, R, anchor, N, lattice);
+  const int RS = lat_row_stride(R);
+  const size_t lds = (size_t)2 * kTopK * RS * sizeof(uint16_t) + (size_t)RS * sizeof(float);
+  const bool vec = R % 8 == 0 && aligned(pred_cb, 16) && aligned(succ_cb, 16) && aligned(gate, 16);
+  if (vec)
+    select_lattice_kernel<true><<<dim3(N, B), 256, lds, stream>>>(cand_idx, cand_val, gate, pred_cb,
+                                                                 succ_cb, V, R, anchor, N, lattice);
+  else
+    select_lattice_kernel<false><<<dim3(N, B), 256, lds, stream>>>(cand_idx, cand_val, gate, pred_cb,
+                                                                  succ_cb, V, R, anchor, N, lattice);
   select_path_kernel<<<B, 64, 0, stream>>>(cand_idx, cand_val, V, anchor, temperature, seed, step,
                                            N, lattice, tokens, slot, q, status);
   return launch_status();

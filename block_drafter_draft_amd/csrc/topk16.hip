@@ -19,80 +19,8 @@
 namespace df2 {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = kChunkThreads;
 constexpr int kCap = 512;  // candidate slots in LDS
-
-template <class KT, int EPT>
-struct ChunkLoad {
-  using E = typename KT::elem_t;
-  static constexpr int kEPV = 16 / (int)sizeof(E);  // elements per 16-byte vector
-  static constexpr int kNV = EPT / kEPV;              // vectors per thread
-};
-
-// element e of thread t lives at chunk offset (e / EPV) * 256 * EPV + t * EPV + e % EPV
-template <int EPV>
-__device__ __forceinline__ int elem_offset(int t, int e) {
-  return (e / EPV) * (kThreads * EPV) + t * EPV + (e % EPV);
-}
-
-template <class KT, int EPT, bool VEC>
-__device__ __forceinline__ void load_chunk(const typename KT::elem_t* __restrict__ row, int base,
-                                           int V, uint32_t (&bits)[EPT]) {
-  using E = typename KT::elem_t;
-  const int t = threadIdx.x;
-  if constexpr (VEC) {
-    constexpr int EPV = ChunkLoad<KT, EPT>::kEPV;
-#pragma unroll
-    for (int v = 0; v < EPT / EPV; ++v) {
-      int off = base + v * (kThreads * EPV) + t * EPV;
-      if (off + EPV <= V) {
-        const u32x4_t w = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + off));
-        const uint32_t ws[4] = {w[0], w[1], w[2], w[3]};
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-          if constexpr (sizeof(E) == 2)
-            bits[v * EPV + e] = (ws[e / 2] >> (16 * (e & 1))) & 0xffffu;
-          else
-            bits[v * EPV + e] = ws[e];
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-          int x = off + e;
-          uint32_t u = 0;
-          if (x < V) {
-            if constexpr (sizeof(E) == 2)
-              u = reinterpret_cast<const uint16_t*>(row)[x];
-            else
-              u = __float_as_uint(reinterpret_cast<const float*>(row)[x]);
-          }
-          bits[v * EPV + e] = u;
-        }
-      }
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      int x = base + e * kThreads + t;
-      uint32_t u = 0;
-      if (x < V) {
-        if constexpr (sizeof(E) == 2)
-          u = reinterpret_cast<const uint16_t*>(row)[x];
-        else
-          u = __float_as_uint(reinterpret_cast<const float*>(row)[x]);
-      }
-      bits[e] = u;
-    }
-  }
-}
-
-template <int EPT, bool VEC, class KT>
-__device__ __forceinline__ int index_of(int base, int e) {
-  if constexpr (VEC)
-    return base + elem_offset<ChunkLoad<KT, EPT>::kEPV>(threadIdx.x, e);
-  else
-    return base + e * kThreads + threadIdx.x;
-}
 
 // Workgroup maximum of a packed word (all threads must call).
 __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* red) {
@@ -126,7 +54,10 @@ __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(
   __shared__ int count;
 
   uint32_t bits[EPT];
-  load_chunk<KT, EPT, VEC>(row, base, V, bits);
+  if (VEC && base + CH <= V)
+    load_chunk_full<KT, EPT>(row, base, bits);
+  else
+    load_chunk<KT, EPT, VEC>(row, base, V, bits);
 
   // raw keys; lane maximum; detection of NaN / infinities (valid elements only)
   uint32_t key[EPT];
@@ -236,11 +167,19 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
     __syncthreads();
   }
   const uint64_t T = thr;
-  for (int i = threadIdx.x; i < n; i += kThreads) {
-    uint64_t v = src[i];
-    if (v != 0 && v >= T) {
-      int pos = atomicAdd(&count, 1);
-      if (pos < kTopK * kTopK) cand[pos] = v;
+  for (int i0 = 0; i0 < n; i0 += kThreads * 8) {
+    uint64_t vals[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + threadIdx.x + kThreads * u;
+      vals[u] = i < n ? src[i] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (vals[u] != 0 && vals[u] >= T) {
+        int pos = atomicAdd(&count, 1);
+        if (pos < kTopK * kTopK) cand[pos] = vals[u];
+      }
     }
   }
   __syncthreads();

@@ -17,7 +17,7 @@
 namespace df2 {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = kChunkThreads;
 constexpr int kMaxN = 15;
 
 struct ChainRec {
@@ -107,7 +107,7 @@ __device__ void accept_chain(const float* __restrict__ tgt, int64_t row_stride, 
   __syncthreads();
 }
 
-template <class KT, int EPT>
+template <class KT, int EPT, bool VEC>
 __global__ __launch_bounds__(kThreads) void verify_rows_kernel(
     const typename KT::elem_t* __restrict__ target, int64_t seq_stride, int64_t row_stride, int V,
     const int32_t* __restrict__ tokens, const int32_t* __restrict__ cidx,
@@ -115,10 +115,11 @@ __global__ __launch_bounds__(kThreads) void verify_rows_kernel(
     const float* __restrict__ temperature, uint64_t seed, uint64_t step, int N, int nchunks,
     Ws ws) {
   constexpr int CH = EPT * kThreads;
+  constexpr int kRowGroup = 8;  // rows whose loads are issued together
   const int chunk = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const int base = chunk * CH;
   __shared__ ChainRec rec;
-  __shared__ uint64_t red[kThreads / 64][2];
+  __shared__ uint64_t red[kThreads / 64][kRowGroup];
   __shared__ int redf[kThreads / 64];
 
   int st = 0;
@@ -129,29 +130,47 @@ __global__ __launch_bounds__(kThreads) void verify_rows_kernel(
   const typename KT::elem_t* tb = target + (int64_t)b * seq_stride;
 
   if (mode == 0) {
-    // greedy: chunk maximum of every row (elements visited in increasing index per thread)
-    for (int r = 0; r <= N; ++r) {
-      const typename KT::elem_t* row = tb + (int64_t)r * row_stride;
-      uint32_t bk = 0, bi = 0;
+    // greedy: the chunk maximum of every row, eight rows per round of loads
+    for (int r0 = 0; r0 <= N; r0 += kRowGroup) {
+      uint32_t bits[kRowGroup][EPT];
+      // rows past N re-read row N (ignored below), so the loads carry no conditions
+      if (VEC && base + CH <= V) {
 #pragma unroll
-      for (int e = 0; e < EPT; ++e) {
-        const int x = base + t * EPT + e;
-        if (x < V) {
-          const uint32_t k = KT::canon(load_bits<KT>(row, x));
-          if (k > bk) {
-            bk = k;
-            bi = (uint32_t)x;
-          }
+        for (int rr = 0; rr < kRowGroup; ++rr) {
+          const int r = r0 + rr <= N ? r0 + rr : N;
+          load_chunk_full<KT, EPT>(tb + (int64_t)r * row_stride, base, bits[rr]);
+        }
+      } else {
+#pragma unroll
+        for (int rr = 0; rr < kRowGroup; ++rr) {
+          const int r = r0 + rr <= N ? r0 + rr : N;
+          load_chunk<KT, EPT, VEC>(tb + (int64_t)r * row_stride, base, V, bits[rr]);
         }
       }
-      uint64_t m = bk ? pack_cand(bk, bi) : 0ull;
-      m = wave_max_u64(m);
-      if ((t & 63) == 0) red[t >> 6][0] = m;
+#pragma unroll
+      for (int rr = 0; rr < kRowGroup; ++rr) {
+        uint64_t m = 0;
+        if (r0 + rr <= N) {
+          uint32_t bk = 0, bi = 0;
+#pragma unroll
+          for (int e = 0; e < EPT; ++e) {
+            const int x = index_of<EPT, VEC, KT>(base, e);
+            const uint32_t k = x < V ? KT::canon(bits[rr][e]) : 0u;
+            if (k > bk) {
+              bk = k;
+              bi = (uint32_t)x;
+            }
+          }
+          m = bk ? pack_cand(bk, bi) : 0ull;
+        }
+        m = wave_max_u64(m);
+        if ((t & 63) == 0) red[t >> 6][rr] = m;
+      }
       __syncthreads();
-      if (t == 0) {
-        uint64_t g = red[0][0];
-        for (int w = 1; w < kThreads / 64; ++w) g = red[w][0] > g ? red[w][0] : g;
-        ws.best[((int64_t)b * (N + 1) + r) * nchunks + chunk] = g;
+      if (t < kRowGroup && r0 + t <= N) {
+        uint64_t g = red[0][t];
+        for (int w = 1; w < kThreads / 64; ++w) g = red[w][t] > g ? red[w][t] : g;
+        ws.best[((int64_t)b * (N + 1) + r0 + t) * nchunks + chunk] = g;
       }
       __syncthreads();
     }
@@ -164,12 +183,17 @@ __global__ __launch_bounds__(kThreads) void verify_rows_kernel(
   if (chunk == 0 && t == 0) ws.chain[b] = rec;
   const float* row = tgt + (int64_t)(rec.pos - 1) * row_stride;
 
+  uint32_t bits[EPT];
+  if (VEC && base + CH <= V)
+    load_chunk_full<KT, EPT>(reinterpret_cast<const typename KT::elem_t*>(row), base, bits);
+  else
+    load_chunk<KT, EPT, VEC>(reinterpret_cast<const typename KT::elem_t*>(row), base, V, bits);
   uint64_t zp = 0;
   int fl = 0;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
-    const int x = base + t * EPT + e;
-    if (x < V) zp += quant40(prob_ok(row[x], &fl));
+    const int x = index_of<EPT, VEC, KT>(base, e);
+    if (x < V) zp += quant40(prob_ok(__uint_as_float(bits[e]), &fl));
   }
   // residual corrections for the candidates of slot pos that fall in this chunk; for a
   // repeated index only its first occurrence counts
@@ -434,43 +458,43 @@ __global__ __launch_bounds__(kThreads) void verify_finish_kernel(
   }
 }
 
+constexpr int kEPT = 8;  // elements per thread: one 16-byte bf16 vector or two f32 vectors
+
 struct Plan {
-  int ept;
   int nchunks;
+  bool vec;
 };
 
-Plan make_plan(int B, int V) {
+Plan make_plan(int V, int dtype, const void* target, int64_t ss, int64_t rs) {
   Plan p;
-  int ept = 16;
-  while (ept > 4 && (int64_t)B * ((V + ept * kThreads - 1) / (ept * kThreads)) < 512) ept >>= 1;
-  p.ept = ept;
-  p.nchunks = (V + ept * kThreads - 1) / (ept * kThreads);
+  p.nchunks = (V + kEPT * kThreads - 1) / (kEPT * kThreads);
+  const int esz = dtype == DFLASH2_BF16 ? 2 : 4;
+  p.vec = (target == nullptr || aligned(target, 16)) && (ss * esz) % 16 == 0 && (rs * esz) % 16 == 0;
   return p;
 }
 
-template <class KT, int EPT>
+template <class KT, bool VEC>
 void launch(const Plan& p, const void* target, int64_t ss, int64_t rs, int V,
             const int32_t* tokens, const int32_t* cidx, const float* q, const int32_t* slot,
             const float* temp, uint64_t seed, uint64_t step, int B, int N, Ws w, int32_t* n_acc,
             int32_t* out, int32_t* status, hipStream_t st) {
   using E = typename KT::elem_t;
-  verify_rows_kernel<KT, EPT><<<dim3(p.nchunks, B), kThreads, 0, st>>>(
+  verify_rows_kernel<KT, kEPT, VEC><<<dim3(p.nchunks, B), kThreads, 0, st>>>(
       (const E*)target, ss, rs, V, tokens, cidx, q, slot, temp, seed, step, N, p.nchunks, w);
-  verify_finish_kernel<KT, EPT><<<B, kThreads, 0, st>>>((const E*)target, ss, rs, V, tokens, cidx,
-                                                        q, temp, seed, step, N, p.nchunks, w,
-                                                        n_acc, out, status);
+  verify_finish_kernel<KT, kEPT><<<B, kThreads, 0, st>>>((const E*)target, ss, rs, V, tokens, cidx,
+                                                         q, temp, seed, step, N, p.nchunks, w,
+                                                         n_acc, out, status);
 }
 
 template <class KT>
-void launch_ept(const Plan& p, const void* target, int64_t ss, int64_t rs, int V,
+void launch_vec(const Plan& p, const void* target, int64_t ss, int64_t rs, int V,
                 const int32_t* tokens, const int32_t* cidx, const float* q, const int32_t* slot,
                 const float* temp, uint64_t seed, uint64_t step, int B, int N, Ws w,
                 int32_t* n_acc, int32_t* out, int32_t* status, hipStream_t st) {
-  switch (p.ept) {
-    case 16: launch<KT, 16>(p, target, ss, rs, V, tokens, cidx, q, slot, temp, seed, step, B, N, w, n_acc, out, status, st); break;
-    case 8: launch<KT, 8>(p, target, ss, rs, V, tokens, cidx, q, slot, temp, seed, step, B, N, w, n_acc, out, status, st); break;
-    default: launch<KT, 4>(p, target, ss, rs, V, tokens, cidx, q, slot, temp, seed, step, B, N, w, n_acc, out, status, st); break;
-  }
+  if (p.vec)
+    launch<KT, true>(p, target, ss, rs, V, tokens, cidx, q, slot, temp, seed, step, B, N, w, n_acc, out, status, st);
+  else
+    launch<KT, false>(p, target, ss, rs, V, tokens, cidx, q, slot, temp, seed, step, B, N, w, n_acc, out, status, st);
 }
 
 }  // namespace
@@ -480,8 +504,7 @@ using namespace df2;
 
 extern "C" size_t dflash2_verify_workspace_bytes(int B, int N, int V, int dtype) {
   if (B < 1 || N < 1 || N > kMaxN || V < kTopK) return 0;
-  (void)dtype;
-  Plan p = make_plan(B, V);
+  Plan p = make_plan(V, dtype, nullptr, 0, 0);
   return ws_layout(B, N, p.nchunks, nullptr, nullptr);
 }
 
@@ -498,14 +521,14 @@ extern "C" int dflash2_verify(const void* target, int dtype, int64_t seq_stride,
   if (dtype != DFLASH2_BF16 && dtype != DFLASH2_F32) return DFLASH2_EUNSUPPORTED;
   if (!aligned(ws, kWsAlign) || ws_bytes < dflash2_verify_workspace_bytes(B, N, V, dtype))
     return DFLASH2_EWORKSPACE;
-  Plan p = make_plan(B, V);
+  Plan p = make_plan(V, dtype, target, seq_stride, row_stride);
   Ws w;
   ws_layout(B, N, p.nchunks, &w, (char*)ws);
   if (dtype == DFLASH2_BF16)
-    launch_ept<KeyBF16>(p, target, seq_stride, row_stride, V, tokens, cand_idx, q, slot,
+    launch_vec<KeyBF16>(p, target, seq_stride, row_stride, V, tokens, cand_idx, q, slot,
                         temperature, seed, step, B, N, w, n_accept, out_tokens, status, stream);
   else
-    launch_ept<KeyF32>(p, target, seq_stride, row_stride, V, tokens, cand_idx, q, slot,
+    launch_vec<KeyF32>(p, target, seq_stride, row_stride, V, tokens, cand_idx, q, slot,
                        temperature, seed, step, B, N, w, n_accept, out_tokens, status, stream);
   return launch_status();
 }

@@ -69,7 +69,7 @@ def test_workspace_sizes():
     V = 248320
     for B in (1, 16, 64):
         a = L.dflash2_block_attn_workspace_bytes(B, 8, 32, 8, 128, 2048, 2048, d2.BF16)
-        assert a > 0 and a % 256 == 0
+        assert a % 256 == 0 and (a > 0 or B == 64)   # one split per head needs none
         t = L.dflash2_topk16_workspace_bytes(B, 7, V, d2.BF16)
         assert t >= B * 7 * 16 * 8 and t % 256 == 0
         s = L.dflash2_select_workspace_bytes(B, 7)
