@@ -641,3 +641,34 @@ def test_verify_one_hot_target_sampled_equals_greedy(orc):
     s = orc.verify(target, B, N, (N + 1) * V, V, V, d, ci, q, slot, np.ones(B, np.float32), 5, 0)
     for a, b_ in zip(g, s):
         np.testing.assert_array_equal(a, b_)
+
+
+# ----------------------------------------------------------------------------------------
+# Printed live key counts ("Geramy/LSE docs/DFLASH2.md", native-test notes)
+# ----------------------------------------------------------------------------------------
+
+def _golden_rows(name):
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", name)
+    rows = []
+    for line in open(path):
+        line = line.split("#", 1)[0].strip()
+        if line:
+            rows.append([int(x) for x in line.split()])
+    return rows
+
+
+def test_attention_live_counts_printed_on_the_pages(orc):
+    # With zero queries every visible key gets the same weight 1/live. Value column 0 is 1
+    # on block keys only, so the anchor's output there is P/live: the live count read back.
+    for L, W, P, D, live in _golden_rows("lse_live_context_counts.txt"):
+        S = max(W, 16)
+        q = np.zeros((1, P, 1, D), np.float32)
+        kb = np.zeros((1, P, 1, D), np.float32)
+        kr = np.zeros((1, S, 1, D), np.float32)
+        vb = np.zeros((1, P, 1, D), np.float32)
+        vr = np.zeros((1, S, 1, D), np.float32)
+        vb[..., 0] = 1.0
+        out = orc.block_attn(q, kb, vb, kr, vr, np.array([L], np.int32), W)
+        got = P / out[0, 0, 0, 0]
+        assert abs(got - live) < 1e-9, (L, W, got, live)
