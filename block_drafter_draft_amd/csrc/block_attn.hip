@@ -32,6 +32,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kRows = 32;    // query rows per tile
+constexpr int kMaxSplits = 32;  // most splits of one (sequence, KV head)
 constexpr int kStage = 64;   // keys per stage (two 32-key tiles)
 
 // Split planning: aim for kAttnTargetWGs workgroups, with at least kAttnMinStages stages
@@ -307,12 +308,277 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
   if (dh == 0 && hh == 0) ws_ml[part * kRows + n] = make_float2(m, l);
 }
 
+// ---------------------------------------------------------------------------------------
+// D = 128 streaming kernel. The keys of one (sequence, KV head) are listed as the visible
+// context window (oldest first) followed by the P block keys, and cut into 32-key tiles.
+// A workgroup owns a contiguous range of tiles (one split); each of its four waves takes
+// every fourth tile and works on its own: it streams the tile's K and V rows (8 KiB each)
+// straight from HBM into its own pair of LDS buffers with global_load_lds (16 bytes per
+// lane, no registers held while the load is in flight), the next tile's copy overlapping
+// the current tile's arithmetic, so no barrier is needed until the end. Per tile a wave
+// computes S^T = K Q^T (8 MFMA 32x32x16), the online softmax in-lane, and O^T += V^T P^T
+// for all 128 columns (8 MFMA), with the V^T operand read by ds_read_b64_tr_b16, which
+// hands each lane four keys of one column. Rows land in LDS with their 16-byte chunks
+// XOR-swizzled by the row index, so that both the K reads (16 rows, one chunk) and the
+// transposed V reads (4 rows, 4 chunks per half-wave) hit distinct banks. At the end the
+// four waves' states are merged through LDS, each wave producing a quarter of the columns.
+constexpr int kTileKeys = 32;
+#ifndef DF2_STREAM_WAVES
+#define DF2_STREAM_WAVES 4
+#endif
+constexpr int kStreamWaves = DF2_STREAM_WAVES;  // waves per workgroup
+constexpr int kStreamD = 128;
+constexpr int kTileElems = kTileKeys * kStreamD;     // one tensor's tile (8 KiB of bf16)
+constexpr int kMergeStride = 40;                      // floats per d row of a merge state
+
+#define DF2_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+struct StreamSmem {
+  union {
+    uint16_t kv[kStreamWaves][2][2][kTileElems];           // [wave][buffer][K, V][tile]
+    float o[kStreamWaves][kStreamD][kMergeStride];         // [wave][d][query row]
+  };
+  float m[kStreamWaves][kRows], l[kStreamWaves][kRows];
+};
+
+// chunk swizzle of tile row r: 16 consecutive rows get 16 distinct values, and 4
+// consecutive rows (aligned to 4) land in 4 different groups of four chunks
+__device__ __forceinline__ int tile_swz(int r) { return ((r & 3) << 2) ^ ((r >> 2) & 3); }
+
+__global__ __launch_bounds__(64 * kStreamWaves) void attn_stream_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kb,
+    const uint16_t* __restrict__ vb, const uint16_t* __restrict__ kr,
+    const uint16_t* __restrict__ vr, const int32_t* __restrict__ ctx_len, int P, int Hq, int Hkv,
+    int S, int W, float scale_log2, int nsplit, int tiles_per_split, float* __restrict__ ws_o,
+    float2* __restrict__ ws_ml, uint16_t* __restrict__ out) {
+  constexpr int D = kStreamD;
+  __shared__ StreamSmem sm;
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63, n = lane & 31, hh = lane >> 5;
+  const int G = Hq / Hkv, rows = P * G;
+  int L = ctx_len[b];
+  L = L < 0 ? 0 : L;
+  const int lo = L - W + 1 > 0 ? L - W + 1 : 0;   // oldest visible context position
+  const int nctx = L - lo;                         // context keys in the list
+  const int nkeys = nctx + P;
+  const int ntiles = (nkeys + kTileKeys - 1) / kTileKeys;
+  const int tbeg = split * tiles_per_split;
+  int tend = tbeg + tiles_per_split;
+  tend = tend < ntiles ? tend : ntiles;
+  // this wave's tiles: tbeg + w, tbeg + w + 4, ...
+  const int nmine = tend - tbeg - w > 0 ? (tend - tbeg - w + kStreamWaves - 1) / kStreamWaves : 0;
+
+  // Q^T as the B operand: lane (n, hh) holds q[n][16 ks + 8 hh .. +7]
+  const bool qvalid = n < rows;
+  const int slot_n = qvalid ? n / G : 0;
+  const int head_n = g * G + (qvalid ? n % G : 0);
+  const uint16_t* qrow = q + (((int64_t)b * P + slot_n) * Hq + head_n) * D;
+  bf16x8_t qop[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    u32x4_t v = qvalid ? ld16(qrow + 16 * ks + 8 * hh) : u32x4_t{0, 0, 0, 0};
+    qop[ks] = __builtin_bit_cast(bf16x8_t, v);
+  }
+  // list index of this query's oldest visible context key (block keys are always visible)
+  const int kmin = L + slot_n - W + 1 - lo;
+
+  // Copy of tile `tile` into buffer `buf`: instruction i moves rows 4i .. 4i+3; lane l
+  // fetches chunk (l & 15) ^ swz(row) of row 4i + l / 16 into LDS slot l.
+  const int64_t ring_b = (int64_t)b * S * Hkv * D + (int64_t)g * D;
+  const int64_t blk_b = (int64_t)b * P * Hkv * D + (int64_t)g * D;
+  const int lrow = lane >> 4;
+  auto issue = [&](int tile, int buf) {
+    const int kk0 = tile * kTileKeys;
+    const int jm = kk0 < nctx ? (lo + kk0) % S : 0;  // ring row of list entry kk0 (if context)
+    const uint16_t* ksrc[8];
+    const uint16_t* vsrc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + lrow;
+      const int kk = kk0 + r;
+      int jr = jm + r;
+      if (S >= kTileKeys) {
+        jr = jr >= S ? jr - S : jr;
+      } else {
+        jr = jr % S;
+      }
+      const int p = kk - nctx >= 0 && kk - nctx < P ? kk - nctx : 0;  // padding: block row 0
+      const bool ctx = kk < nctx;
+      const int64_t roff = ctx ? ring_b + (int64_t)jr * Hkv * D : blk_b + (int64_t)p * Hkv * D;
+      const int64_t coff = 8 * ((lane & 15) ^ tile_swz(r));
+      ksrc[i] = (ctx ? kr : kb) + (roff + coff);
+      vsrc[i] = (ctx ? vr : vb) + (roff + coff);
+    }
+    uint16_t* dk = &sm.kv[w][buf][0][0];
+    uint16_t* dv = &sm.kv[w][buf][1][0];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_global_load_lds((const void*)ksrc[i], DF2_LDS(dk + i * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)vsrc[i], DF2_LDS(dv + i * 512), 16, 0, 0);
+    }
+  };
+
+  float m = -INFINITY, l = 0.0f;
+  f32x16_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = f32x16_t{};
+
+  auto compute = [&](int tile, int buf) {
+    const uint16_t* tk = &sm.kv[w][buf][0][0];
+    const uint16_t* tv = &sm.kv[w][buf][1][0];
+    // S^T: accumulator i of lane (n, hh) is tile key 8(i/4) + 4hh + i%4
+    f32x16_t s = f32x16_t{};
+    const int swn = tile_swz(n);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const int c = (2 * ks + hh) ^ swn;
+      const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(tk + n * D + 8 * c);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv), qop[ks], s, 0,
+                                                 0, 0);
+    }
+    const int kk0 = tile * kTileKeys;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int kk = kk0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+      const bool vis = kk < nctx ? kk >= kmin : kk < nkeys;
+      s[i] = vis ? s[i] * scale_log2 : -INFINITY;
+      mx = fmaxf(mx, s[i]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mnew = fmaxf(m, mx);
+    const float base = mnew == -INFINITY ? 0.0f : mnew;
+    const float alpha = exp2f(m - base);
+    float psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s[i] = exp2f(s[i] - base);
+      psum += s[i];
+    }
+    psum += __shfl_xor(psum, 32, 64);
+    l = l * alpha + psum;
+    m = mnew;
+    bf16x8_t pb[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[u][e] = (__bf16)s[8 * u + e];
+    // V^T operand of k-step u, d tile dt: lane (j = lane & 15 of group gq) points at row
+    // 16u + 8 iota + 4hh + j/4, columns 32 dt + 16 (gq & 1) + 4 (j & 3) .. +3. The reads are
+    // issued as inline assembly and waited for explicitly: their ordering behind this
+    // tile's copy is already established by the vmcnt wait above.
+    const int gq = lane >> 4, j = lane & 15;
+    const uint32_t tv_base = (uint32_t)reinterpret_cast<uintptr_t>(DF2_LDS(tv));
+    uint64_t vt[4][2][2];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const int d = 32 * dt + 16 * (gq & 1) + 4 * (j & 3);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int io = 0; io < 2; ++io) {
+          const int r = 16 * u + 8 * io + 4 * hh + (j >> 2);
+          const int c = (d >> 3) ^ tile_swz(r);
+          const uint32_t a = tv_base + 2u * (uint32_t)(r * D + 8 * c + (d & 7));
+          asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(vt[dt][u][io]) : "v"(a));
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(vt[0][0][0]), "+v"(vt[0][0][1]), "+v"(vt[0][1][0]), "+v"(vt[0][1][1]),
+                   "+v"(vt[1][0][0]), "+v"(vt[1][0][1]), "+v"(vt[1][1][0]), "+v"(vt[1][1][1]),
+                   "+v"(vt[2][0][0]), "+v"(vt[2][0][1]), "+v"(vt[2][1][0]), "+v"(vt[2][1][1]),
+                   "+v"(vt[3][0][0]), "+v"(vt[3][0][1]), "+v"(vt[3][1][0]), "+v"(vt[3][1][1]));
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      o[dt] *= alpha;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const u32x4_t w4 = {(uint32_t)vt[dt][u][0], (uint32_t)(vt[dt][u][0] >> 32),
+                            (uint32_t)vt[dt][u][1], (uint32_t)(vt[dt][u][1] >> 32)};
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w4), pb[u],
+                                                       o[dt], 0, 0, 0);
+      }
+    }
+  };
+
+  // two tiles in flight from the start; tile k + 2 reuses tile k's buffer once it is read
+  if (nmine > 0) issue(tbeg + w, 0);
+  if (nmine > 1) issue(tbeg + w + kStreamWaves, 1);
+  for (int k = 0; k < nmine; ++k) {
+    const int tile = tbeg + w + kStreamWaves * k;
+    if (k + 1 < nmine)
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // tile k + 1's 16 copies may fly on
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    compute(tile, k & 1);
+    if (k + 2 < nmine) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // tile k's LDS reads have returned
+      issue(tile + 2 * kStreamWaves, k & 1);
+    }
+  }
+
+  // merge: every wave stores its state; wave w then combines columns [32w, 32w + 32)
+  __syncthreads();  // all tile reads are done before the buffers are reused
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int d = 32 * dt + 8 * (r >> 2) + 4 * hh + (r & 3);
+      sm.o[w][d][n] = o[dt][r];
+    }
+  if (hh == 0) {
+    sm.m[w][n] = m;
+    sm.l[w][n] = l;
+  }
+  __syncthreads();
+  float mw[kStreamWaves], M = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < kStreamWaves; ++v) {
+    mw[v] = sm.m[v][n];
+    M = fmaxf(M, mw[v]);
+  }
+  float aw[kStreamWaves], Lsum = 0.0f;
+#pragma unroll
+  for (int v = 0; v < kStreamWaves; ++v) {
+    aw[v] = M == -INFINITY ? 0.0f : exp2f(mw[v] - M);
+    Lsum += aw[v] * sm.l[v][n];
+  }
+  // lane (n, hh): query row n, CPL columns from d0
+  constexpr int CPL = D / kStreamWaves / 2;
+  const int d0 = (D / kStreamWaves) * w + CPL * hh;
+  float acc[CPL];
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) {
+    float a = 0.0f;
+#pragma unroll
+    for (int v = 0; v < kStreamWaves; ++v) a += aw[v] * sm.o[v][d0 + e][n];
+    acc[e] = a;
+  }
+  if (nsplit == 1) {
+    if (!qvalid) return;
+    const float inv = 1.0f / Lsum;
+    uint16_t* dst = out + (((int64_t)b * P + slot_n) * Hq + head_n) * D + d0;
+    u32x4_t pk[CPL / 8];
+#pragma unroll
+    for (int h = 0; h < CPL / 2; ++h)
+      pk[h >> 2][h & 3] = (uint32_t)f32_to_bf16(acc[2 * h] * inv) |
+                          ((uint32_t)f32_to_bf16(acc[2 * h + 1] * inv) << 16);
+#pragma unroll
+    for (int v = 0; v < CPL / 8; ++v) *reinterpret_cast<u32x4_t*>(dst + 8 * v) = pk[v];
+    return;
+  }
+  const int64_t part = ((int64_t)b * Hkv + g) * nsplit + split;
+  float* po = ws_o + (part * kRows + n) * D + d0;
+#pragma unroll
+  for (int e = 0; e < CPL; e += 4)
+    *reinterpret_cast<float4*>(po + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+  if (w == 0 && hh == 0) ws_ml[part * kRows + n] = make_float2(M, Lsum);
+}
+
 // Combines the splits of one (sequence, KV head, quarter of D). The (max, sum) pairs of all
 // splits are read in one parallel batch into LDS and turned into weights; then thread (n, c)
 // (query row n, 4 consecutive columns) issues the loads of all its split partials before
 // using any of them.
-constexpr int kMaxSplits = 32;
-
 template <int D, int MS>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ ws_o,
                                                            const float2* __restrict__ ws_ml, int P,
@@ -454,6 +720,33 @@ SplitPlan plan_splits(int B, int Hkv, int W) {
   return p;
 }
 
+// D = 128 streaming kernel: each workgroup should have at least kStreamMinTiles tiles
+// (one per wave), and a launch about kStreamTargetWGs workgroups (one per compute unit,
+// the LDS buffers allowing one workgroup per unit).
+#ifndef DF2_STREAM_TARGET_WGS
+#define DF2_STREAM_TARGET_WGS 256
+#endif
+#ifndef DF2_STREAM_MIN_TILES
+#define DF2_STREAM_MIN_TILES 4
+#endif
+SplitPlan plan_stream(int B, int Hkv, int P, int W) {
+  const int ntiles = (W - 1 + P + kTileKeys - 1) / kTileKeys;  // tiles of the longest list
+  const int units = B * Hkv;
+  int ns = (DF2_STREAM_TARGET_WGS + units - 1) / units;
+  const int by_tiles = (ntiles + DF2_STREAM_MIN_TILES - 1) / DF2_STREAM_MIN_TILES;
+  ns = ns < by_tiles ? ns : by_tiles;
+  ns = ns < kMaxSplits ? ns : kMaxSplits;
+  ns = ns < 1 ? 1 : ns;
+  SplitPlan p;
+  p.stages_per_split = (ntiles + ns - 1) / ns;  // tiles per split
+  p.nsplit = (ntiles + p.stages_per_split - 1) / p.stages_per_split;
+  return p;
+}
+
+SplitPlan plan_for(int B, int Hkv, int P, int D, int W) {
+  return D == kStreamD ? plan_stream(B, Hkv, P, W) : plan_splits(B, Hkv, W);
+}
+
 }  // namespace
 }  // namespace df2
 
@@ -461,12 +754,11 @@ using namespace df2;
 
 extern "C" size_t dflash2_block_attn_workspace_bytes(int B, int P, int Hq, int Hkv, int D, int S,
                                                      int W, int dtype) {
-  (void)P;
   (void)Hq;
   (void)S;
-  if (B < 1 || Hkv < 1 || W < 1 || (D != 64 && D != 128)) return 0;
+  if (B < 1 || Hkv < 1 || W < 1 || P < 1 || (D != 64 && D != 128)) return 0;
   if (dtype != DFLASH2_BF16) return 0;
-  const SplitPlan sp = plan_splits(B, Hkv, W);
+  const SplitPlan sp = plan_for(B, Hkv, P, D, W);
   if (sp.nsplit == 1) return 0;
   const size_t parts = (size_t)B * Hkv * sp.nsplit;
   return round_up(parts * kRows * D * sizeof(float), kWsAlign) +
@@ -498,15 +790,16 @@ extern "C" int dflash2_block_attn(const void* q, const void* k_blk, const void* 
     if (!aligned(p, 16)) return DFLASH2_EUNSUPPORTED;
   const size_t need = dflash2_block_attn_workspace_bytes(B, P, Hq, Hkv, D, S, W, dtype);
   if (need && (!ws || !aligned(ws, kWsAlign) || ws_bytes < need)) return DFLASH2_EWORKSPACE;
-  const SplitPlan sp = plan_splits(B, Hkv, W);
+  const SplitPlan sp = plan_for(B, Hkv, P, D, W);
   const size_t parts = (size_t)B * Hkv * sp.nsplit;
+  // workspace: partial outputs, then their (max, sum)
   float* ws_o = need ? (float*)ws : nullptr;
   float2* ws_ml =
       need ? (float2*)((char*)ws + round_up(parts * kRows * D * sizeof(float), kWsAlign)) : nullptr;
   const float sl2 = scale * kLog2e;
   dim3 grid(sp.nsplit, Hkv, B);
   if (D == 128) {
-    attn_split_kernel<128><<<grid, 256, 0, stream>>>(
+    attn_stream_kernel<<<grid, 64 * kStreamWaves, 0, stream>>>(
         (const uint16_t*)q, (const uint16_t*)k_blk, (const uint16_t*)v_blk,
         (const uint16_t*)k_ring, (const uint16_t*)v_ring, ctx_len, P, Hq, Hkv, S, W, sl2,
         sp.nsplit, sp.stages_per_split, ws_o, ws_ml, (uint16_t*)out);

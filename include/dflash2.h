@@ -90,6 +90,8 @@ extern "C" {
  * 0 <= j < L_b. Query head h uses KV head h / (Hq / Hkv). Scores are scaled by `scale`
  * (pass 1/sqrt(D) for the usual scaling), softmax in binary32.
  * dtype: DFLASH2_BF16 (MFMA path) or DFLASH2_F32, for all of q, k*, v*, out.
+ * The window may be split across workgroups; the workspace then holds the split partials
+ * and their softmax statistics, which a second kernel combines.
  * Requires B >= 1, 2 <= P <= 16, Hq % Hkv == 0, (Hq / Hkv) * P <= 32 for bf16 (64 for
  * f32), D in {64, 128}, W >= 1, S >= W - 1 (every windowed key is still in the ring),
  * and ctx_len[b] >= 0 (negative values are clamped to 0 on the device).

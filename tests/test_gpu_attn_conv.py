@@ -123,6 +123,25 @@ def test_attn_deterministic(d2):
     np.testing.assert_array_equal(a, b)
 
 
+def test_attn_workspace_reuse(d2):
+    # one workspace (filled with 0xFF first) for several calls of different contexts
+    rng = np.random.default_rng(55)
+    B, P, Hq, Hkv, D, S, W = 2, 8, 32, 8, 128, 2048, 2048
+    need = d2.block_attn_workspace_bytes(B, P, Hq, Hkv, D, S, W, d2.BF16)
+    assert need > 0
+    ws = d2.workspace(need, "cuda:0")
+    ws.fill_(0xFF)
+    for call, L in enumerate(([3000, 17], [2047, 0], [5, 9000])):
+        q, kb, vb, kr, vr = _rand_attn(rng, B, P, Hq, Hkv, D, S)
+        say(f"block_attn workspace reuse call {call} L={L}")
+        out = poison_like(q.shape, torch.bfloat16)
+        d2.block_attn(to_dev(q), to_dev(kb), to_dev(vb), to_dev(kr), to_dev(vr),
+                      to_dev(np.asarray(L, np.int32)), W, out=out, ws=ws)
+        torch.cuda.synchronize()
+        ref = orc.block_attn(q, kb, vb, kr, vr, np.asarray(L, np.int32), W)
+        assert_close_tol(to_host(out), ref, what=f"reuse call {call}", **BF16_TOL)
+
+
 # ------------------------------------------------------------------------------------------
 # dynconv2
 # ------------------------------------------------------------------------------------------
