@@ -2,196 +2,408 @@
 // paragraph: equal scores go to the smaller index, NaNs first by index, infinities keep
 // their normal order).
 //
-// A row is cut into chunks; one 256-thread workgroup reads one chunk once from HBM with
-// 16-byte loads and keeps it in registers, finds the chunk's own top-16, and writes it as
-// 16 packed (key, ~index) words. A second kernel merges the chunk lists of a row. The
-// union of the chunk top-16 lists holds the row's top-16 (the order is total), so the
-// result is exact.
+// A row is cut into wave sub-chunks of 64 x EPT elements, dealt round-robin over the
+// waves of the row's workgroups (four waves each), so the workgroups of a row move
+// through it side by side. Each wave works on its own, with no workgroup barrier: it
+// streams its sub-chunks from HBM straight into its own three LDS buffers with
+// global_load_lds (16 bytes per lane), two sub-chunks in flight while the third is
+// examined, and keeps its own running candidate list in LDS. Every wave writes the 16
+// best of its list as 16 packed (key, ~index) words; the union of a row's lists holds the
+// row's top-16 (the order is total), and a second kernel merges them into the exact
+// answer. The larger packed word comes first, so ties go to the lower index.
 //
-// Chunk top-16, fast path: every lane takes the maximum key of its elements; each wave
-// sorts its 64 lane maxima and takes the 16th, and the workgroup threshold T is the
-// largest of the four. At least 16 elements have a key >= T, so every top-16 element has
-// a key >= T. The few elements at or above T are compacted into LDS and each one's rank is
-// counted directly. Slow path (NaN or ±inf present, or too many candidates, e.g. a row of
-// equal values): 16 rounds of a workgroup-wide maximum of packed words.
+// Candidates are admitted by a threshold key T: every top-16 element of the wave's share
+// has a key >= T. On the first sub-chunk T is the 16th largest lane maximum (at least 16
+// elements reach it), found by a 16- or 32-step bitwise search on ballots; whenever the
+// list grows long it is cut to its 16 best and T rises to the 16th best key, so later
+// sub-chunks admit almost nothing. A sub-chunk holding NaN or an infinity (or overflowing
+// the list) is instead reduced exactly, by 16 rounds of a wave maximum of packed words
+// over canonical keys, and its 16 best appended.
 #include "common.hpp"
 
 namespace df2 {
 namespace {
 
 constexpr int kThreads = kChunkThreads;
-constexpr int kCap = 512;  // candidate slots in LDS
 
-// Workgroup maximum of a packed word (all threads must call).
-__device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* red) {
-  v = wave_max_u64(v);
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __syncthreads();
-  if (lane == 0) red[w] = v;
-  __syncthreads();
-  uint64_t m = red[0];
+#define DF2_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// the 16th largest of the wave's 64 values (bitwise search on ballots; all lanes call)
+template <int KB>
+__device__ __forceinline__ uint32_t wave_kth16(uint32_t v) {
+  uint32_t prefix = 0;
 #pragma unroll
-  for (int i = 1; i < kThreads / 64; ++i) m = red[i] > m ? red[i] : m;
-  return m;
+  for (int bit = KB - 1; bit >= 0; --bit) {
+    const uint32_t c = prefix | (1u << bit);
+    if (__popcll(__ballot(v >= c)) >= kTopK) prefix = c;
+  }
+  return prefix;
 }
 
-template <class KT, int EPT, bool VEC>
-__global__ __launch_bounds__(kThreads) void topk_chunk_kernel(
+constexpr int kWaves = kThreads / 64;
+constexpr int kWCap = 256;      // candidate slots per wave
+constexpr int kReduceAt = 64;   // list length that triggers a cut to the best 16
+constexpr int kBufs = 3;        // LDS buffers per wave (two sub-chunks in flight)
+
+template <class KT, int NV>
+struct WaveSmem {
+  u32x4_t buf[kWaves][kBufs][NV][64];  // [wave][buffer][vector][lane]
+  uint64_t list[kWaves][kWCap];
+  uint64_t top[kWaves][kTopK];
+};
+
+template <class KT, int NV, bool VEC>
+__global__ __launch_bounds__(kThreads) void topk_wave_kernel(
     const typename KT::elem_t* __restrict__ scores, int64_t seq_stride, int64_t row_stride,
-    int row0, int N, int V, int nchunks, uint64_t* __restrict__ ws) {
-  constexpr int CH = EPT * kThreads;
-  const int chunk = blockIdx.x;
-  const int rowid = blockIdx.y;  // b * N + r
+    int row0, int N, int V, int seg_len, int nseg, uint64_t* __restrict__ ws) {
+  using E = typename KT::elem_t;
+  constexpr int EPV = 16 / (int)sizeof(E);
+  constexpr int EPT = NV * EPV;      // elements per lane per sub-chunk
+  constexpr int WCH = 64 * EPT;      // elements per wave sub-chunk
+  constexpr int KB = 8 * (int)sizeof(E);
+  __shared__ WaveSmem<KT, NV> sm;
+  const int seg = blockIdx.x, rowid = blockIdx.y;
   const int b = rowid / N, r = rowid % N;
-  const typename KT::elem_t* row =
-      scores + (int64_t)b * seq_stride + (int64_t)(row0 + r) * row_stride;
-  const int base = chunk * CH;
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const E* row = scores + (int64_t)b * seq_stride + (int64_t)(row0 + r) * row_stride;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // The row's wave sub-chunks are dealt round-robin: sub-chunk j of wave w of segment seg
+  // is the row's sub-chunk (j nseg + seg) 4 + w, so the workgroups of a row move through it
+  // side by side.
+  (void)seg_len;
+  const int s1 = V;
+  const int ntot = (V + WCH - 1) / WCH;
+  const int first = seg * kWaves + w;
+  const int nsub = ntot > first ? (ntot - first + kWaves * nseg - 1) / (kWaves * nseg) : 0;
+  auto wbase = [&](int j) { return ((j * nseg + seg) * kWaves + w) * WCH; };
+  uint64_t* list = sm.list[w];
+  uint64_t* top = sm.top[w];
 
-  __shared__ uint64_t cand[kCap];
-  __shared__ uint64_t red[kThreads / 64];
-  __shared__ uint32_t wthr[kThreads / 64];
-  __shared__ int count;
-
-  uint32_t bits[EPT];
-  if (VEC && base + CH <= V)
-    load_chunk_full<KT, EPT>(row, base, bits);
-  else
-    load_chunk<KT, EPT, VEC>(row, base, V, bits);
-
-  // raw keys; lane maximum; detection of NaN / infinities (valid elements only)
-  uint32_t key[EPT];
-  uint32_t kmax = 0;
-  int special = 0;
+  // copy of sub-chunk j into buffer slot: vector v of lane l holds elements
+  // wb + v * 64 EPV + l EPV .. + EPV - 1 (wb = the sub-chunk start); rows that are not
+  // 16-byte aligned go element by element through registers instead (no copy engine)
+  auto issue = [&](int j, int slot) {
+    const int wb = wbase(j);
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    bool valid = index_of<EPT, VEC, KT>(base, e) < V;
-    uint32_t k = valid ? KT::raw(bits[e]) : 0u;
-    special |= valid && (k <= KT::kNegInf || k >= KT::kPosInf);
-    key[e] = k;
-    kmax = k > kmax ? k : kmax;
-  }
-  if (t == 0) count = 0;
-  const int any_special = __syncthreads_or(special);
+    for (int v = 0; v < NV; ++v) {
+      int off = wb + v * 64 * EPV + lane * EPV;
+      off = off + EPV <= V ? off : V - EPV;  // past the end: re-read the last vector (unused)
+      __builtin_amdgcn_global_load_lds((const void*)(row + off), DF2_LDS(&sm.buf[w][slot][v][0]),
+                                       16, 0, 0);
+    }
+  };
 
-  uint64_t* out = ws + ((int64_t)rowid * nchunks + chunk) * kTopK;
-  bool slow = any_special != 0;
+  uint32_t Tf = 0;  // admission threshold on raw keys
+  int cnt = 0;      // list length (wave-uniform)
 
-  if (!slow) {
-    uint32_t srt = wave_sort_desc_u32(kmax);
-    uint32_t thr = __shfl(srt, 15, 64);
-    if (lane == 0) wthr[wv] = thr;
-    __syncthreads();
-    uint32_t T = wthr[0];
+  // cut the list to its best 16; the threshold rises to the 16th key
+  auto reduce = [&]() {
+    if (lane < kTopK) top[lane] = 0;
+    for (int c = lane; c < cnt; c += 64) {
+      const uint64_t v = list[c];
+      int rank = 0;
+      for (int o = 0; o < cnt; ++o) rank += list[o] > v;
+      if (rank < kTopK) top[rank] = v;
+    }
+    if (lane < kTopK) list[lane] = top[lane];
+    if (cnt >= kTopK) {
+      const uint32_t T = cand_key(list[kTopK - 1]);
+      Tf = T == KT::kPosZero ? T - 1 : T;  // -0 ranks equal to +0
+    }
+    cnt = cnt < kTopK ? cnt : kTopK;
+  };
+
+  // any sub-chunk, element by element (partial sub-chunks, f32 rows)
+  auto process_any = [&](const uint32_t (&bits)[EPT], int j) {
+    const int wb = wbase(j);
+    uint32_t key[EPT];
+    uint32_t kmax = 0, valid = 0;
+    bool special = false;
 #pragma unroll
-    for (int i = 1; i < kThreads / 64; ++i) T = wthr[i] > T ? wthr[i] : T;
-    // -0 has a raw key one below +0 but ranks equal to it
-    uint32_t Tf = (T == KT::kPosZero) ? T - 1 : T;
-    if (kmax >= Tf) {
+    for (int e = 0; e < EPT; ++e) {
+      const int x = wb + (e / EPV) * 64 * EPV + lane * EPV + (e % EPV);
+      const bool ok = x < s1;
+      uint32_t k = KT::raw(bits[e]);
+      k = ok ? k : 0u;
+      valid |= (uint32_t)ok << e;
+      special |= ok && (k <= KT::kNegInf || k >= KT::kPosInf);
+      key[e] = k;
+      kmax = k > kmax ? k : kmax;
+    }
+    const bool any_special = __ballot(special) != 0;
+    if (j == 0) {
+      const uint32_t T = wave_kth16<KB>(kmax);
+      Tf = T == KT::kPosZero ? T - 1 : T;
+    }
+    const int cnt0 = cnt;
+    if (!any_special) {
+      const uint64_t below = (1ull << lane) - 1;
 #pragma unroll
       for (int e = 0; e < EPT; ++e) {
-        int x = index_of<EPT, VEC, KT>(base, e);
-        if (x < V && key[e] >= Tf) {
-          uint32_t k = key[e] == KT::kNegZeroRaw ? KT::kPosZero : key[e];
-          int pos = atomicAdd(&count, 1);
-          if (pos < kCap) cand[pos] = pack_cand(k, (uint32_t)x);
+        const bool take = ((valid >> e) & 1u) && key[e] >= Tf;
+        const uint64_t m = __ballot(take);
+        if (m) {
+          const int pos = cnt + __popcll(m & below);
+          if (take && pos < kWCap) {
+            const int x = wb + (e / EPV) * 64 * EPV + lane * EPV + (e % EPV);
+            const uint32_t k = key[e] == KT::kNegZeroRaw ? KT::kPosZero : key[e];
+            list[pos] = pack_cand(k, (uint32_t)x);
+          }
+          cnt += __popcll(m);
         }
       }
     }
-    __syncthreads();
-    const int n = count;
-    if (n <= kCap) {
-      if (t >= n && t < kTopK) out[t] = 0;  // slots beyond the number of candidates stay empty
-      for (int c = t; c < n; c += kThreads) {
-        uint64_t v = cand[c];
-        int rank = 0;
-        for (int o = 0; o < n; ++o) rank += cand[o] > v;
-        if (rank < kTopK) out[rank] = v;
+    if (any_special || cnt > kWCap) {
+      // exact top-16 of this sub-chunk on canonical keys, appended after the kept list
+      uint64_t pk[EPT];
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        const int x = wb + (e / EPV) * 64 * EPV + lane * EPV + (e % EPV);
+        pk[e] = x < s1 ? pack_cand(KT::canon(bits[e]), (uint32_t)x) : 0ull;
       }
-      return;
+      for (int k = 0; k < kTopK; ++k) {
+        uint64_t m = 0;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) m = pk[e] > m ? pk[e] : m;
+        const uint64_t g = wave_max_u64(m);
+        if (lane == 0) list[cnt0 + k] = g;  // 0 (no candidate) ranks last
+#pragma unroll
+        for (int e = 0; e < EPT; ++e)
+          if (g != 0 && pk[e] == g) pk[e] = 0;
+      }
+      cnt = cnt0 + kTopK;
+      reduce();
+    } else if (cnt > kReduceAt) {
+      reduce();
     }
-    slow = true;
-  }
+  };
 
-  // slow path: canonical keys, 16 rounds of a workgroup maximum
-  uint64_t pk[EPT];
+  // a whole bf16 sub-chunk: keys of two elements per 32-bit operation (the sign-magnitude
+  // flip of both halves, then packed 16-bit max and min), so the common case costs about
+  // three VALU operations per element; the rare lanes holding a key >= T append after.
+  // returns false when the sub-chunk must go through process_any instead (NaN or an
+  // infinity present, or the list overflowed; the list is then as it was on entry)
+  auto process_bf16 = [&](const u32x4_t (&q)[NV], int j) -> bool {
+    typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+    const int wb = wbase(j);
+    uint32_t key2[NV * 4];
+    u16x2_t mx2 = {0, 0}, mn2 = {0xffff, 0xffff};
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    int x = index_of<EPT, VEC, KT>(base, e);
-    pk[e] = x < V ? pack_cand(KT::canon(bits[e]), (uint32_t)x) : 0ull;
-  }
-  for (int k = 0; k < kTopK; ++k) {
-    uint64_t m = 0;
+    for (int v = 0; v < NV; ++v)
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) m = pk[e] > m ? pk[e] : m;
-    uint64_t g = block_max_u64(m, red);
-    if (t == 0) out[k] = g;
-    if (g != 0) {
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t u = q[v][i];
+        const uint32_t sgn = (u >> 15) & 0x00010001u;
+        const uint32_t k2 = u ^ (0x80008000u | (sgn * 0x7fffu));
+        key2[4 * v + i] = k2;
+        const u16x2_t kk = __builtin_bit_cast(u16x2_t, k2);
+        mx2 = __builtin_elementwise_max(mx2, kk);
+        mn2 = __builtin_elementwise_min(mn2, kk);
+      }
+    const uint32_t kmax = mx2[0] > mx2[1] ? mx2[0] : mx2[1];
+    const uint32_t kmin = mn2[0] < mn2[1] ? mn2[0] : mn2[1];
+    if (__ballot(kmin <= KT::kNegInf || kmax >= KT::kPosInf)) return false;
+    if (j == 0) {
+      const uint32_t T = wave_kth16<KB>(kmax);
+      Tf = T == KT::kPosZero ? T - 1 : T;
+    }
+    if (__ballot(kmax >= Tf) == 0) return true;
+    const int cnt0_fast = cnt;
+    const uint64_t below = (1ull << lane) - 1;
 #pragma unroll
-      for (int e = 0; e < EPT; ++e)
-        if (pk[e] == g) pk[e] = 0;
+    for (int e = 0; e < EPT; ++e) {
+      const uint32_t k = (key2[e / 2] >> (16 * (e & 1))) & 0xffffu;
+      const bool take = kmax >= Tf && k >= Tf;
+      const uint64_t m = __ballot(take);
+      if (m) {
+        const int pos = cnt + __popcll(m & below);
+        if (take && pos < kWCap) {
+          const int x = wb + (e / EPV) * 64 * EPV + lane * EPV + (e % EPV);
+          list[pos] = pack_cand(k == KT::kNegZeroRaw ? KT::kPosZero : k, (uint32_t)x);
+        }
+        cnt += __popcll(m);
+      }
+    }
+    if (cnt > kWCap) {
+      cnt = cnt0_fast;  // the kept list is intact below cnt0_fast
+      return false;
+    }
+    if (cnt > kReduceAt) reduce();
+    return true;
+  };
+
+  // three buffers: sub-chunks j + 1 and j + 2 are in flight while j is examined. Every
+  // iteration issues exactly NV copies (clamped past the end), so "all but the newest
+  // 2 NV copies have landed" means sub-chunk j is in LDS.
+  issue(0, 0);
+  issue(1, 1);
+  for (int j = 0; j < nsub; ++j) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // sub-chunk j - 1's reads are done
+    issue(j + 2, (j + 2) % kBufs);
+    if constexpr (NV == 1)
+      asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else if constexpr (NV == 2)
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    u32x4_t q[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) q[v] = sm.buf[w][j % kBufs][v][lane];
+    const bool whole = wbase(j) + WCH <= s1;
+    bool done = false;
+    if constexpr (sizeof(E) == 2)
+      if (whole) done = process_bf16(q, j);
+    if (!done) {
+      uint32_t bits[EPT];
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          if constexpr (sizeof(E) == 2)
+            bits[v * EPV + e] = (q[v][e / 2] >> (16 * (e & 1))) & 0xffffu;
+          else
+            bits[v * EPV + e] = q[v][e];
+        }
+      process_any(bits, j);
     }
   }
+  // no copy may still be writing this workgroup's LDS when it ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (cnt > 0) reduce();  // the best 16, sorted
+  uint64_t* out = ws + (((int64_t)rowid * nseg + seg) * kWaves + w) * kTopK;
+  if (lane < kTopK) out[lane] = lane < cnt ? list[lane] : 0ull;
 }
 
-// Merge the chunk lists of one row and write the top-16 (index and widened value). Each
-// chunk list is stored best first, so entry 0 is the chunk's maximum. With more than 16
-// chunks, T = the 16th largest chunk maximum bounds the answer from below; only the 16
-// chunks whose maximum is >= T can hold entries >= T, so at most 256 candidates remain.
+// Rows that are not 16-byte aligned (or whose length is not a whole number of 16-byte
+// vectors): the same per-wave search, with elements loaded through registers.
+template <class KT>
+__global__ __launch_bounds__(kThreads) void topk_wave_scalar_kernel(
+    const typename KT::elem_t* __restrict__ scores, int64_t seq_stride, int64_t row_stride,
+    int row0, int N, int V, int seg_len, int nseg, uint64_t* __restrict__ ws) {
+  using E = typename KT::elem_t;
+  constexpr int EPT = 8;
+  constexpr int WCH = 64 * EPT;
+  const int seg = blockIdx.x, rowid = blockIdx.y;
+  const int b = rowid / N, r = rowid % N;
+  const E* row = scores + (int64_t)b * seq_stride + (int64_t)(row0 + r) * row_stride;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int s0 = seg * seg_len;
+  const int s1 = s0 + seg_len < V ? s0 + seg_len : V;
+  // the wave's exact top-16 kept in lanes 0..15 of `best` (sorted), merged per sub-chunk
+  uint64_t best = 0;
+  for (int wb = s0 + w * WCH; wb < s1; wb += kWaves * WCH) {
+    uint64_t pk[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int x = wb + e * 64 + lane;
+      const int xc = x < V ? x : V - 1;
+      uint32_t u;
+      if constexpr (sizeof(E) == 2)
+        u = reinterpret_cast<const uint16_t*>(row)[xc];
+      else
+        u = __float_as_uint(reinterpret_cast<const float*>(row)[xc]);
+      pk[e] = x < s1 ? pack_cand(KT::canon(u), (uint32_t)x) : 0ull;
+    }
+    // 16 rounds of a wave maximum over this sub-chunk and the kept list
+    uint64_t kept = lane < kTopK ? best : 0ull;
+    uint64_t nb = 0;
+    for (int k = 0; k < kTopK; ++k) {
+      uint64_t m = kept;
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) m = pk[e] > m ? pk[e] : m;
+      const uint64_t g = wave_max_u64(m);
+      if (lane == k) nb = g;
+      if (g != 0) {
+        if (kept == g) kept = 0;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e)
+          if (pk[e] == g) pk[e] = 0;
+      }
+    }
+    best = nb;
+  }
+  uint64_t* out = ws + (((int64_t)rowid * nseg + seg) * kWaves + w) * kTopK;
+  if (lane < kTopK) out[lane] = best;
+}
+
+// Merge the lists of one row (16 packed words each, best first) and write the top-16
+// (index and widened value). A threshold key Tk is found first: each thread takes the
+// largest key among its lists' maxima, and Tk is the largest over the waves of the 16th
+// largest of those (ballot search), so at least 16 list maxima reach it and every top-16
+// entry has a key >= Tk. Only lists whose maximum reaches Tk are read, and their entries
+// with a key >= Tk are ranked directly. If ties make that set too large, the exact 16th
+// largest list maximum T is used instead: at most 16 lists have a maximum >= T.
+constexpr int kMCap = 512;
+
 template <class KT>
 __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
     const typename KT::elem_t* __restrict__ scores, int64_t seq_stride, int64_t row_stride,
-    int row0, int N, int nchunks, const uint64_t* __restrict__ ws, int32_t* __restrict__ idx,
+    int row0, int N, int nlists, const uint64_t* __restrict__ ws, int32_t* __restrict__ idx,
     float* __restrict__ val) {
-  extern __shared__ uint64_t cmax[];  // nchunks chunk maxima
-  __shared__ uint64_t cand[kTopK * kTopK];
+  extern __shared__ uint64_t cmax[];  // nlists list maxima
+  __shared__ uint64_t cand[kMCap];
+  __shared__ uint32_t wthr[kWaves];
   __shared__ uint64_t thr;
   __shared__ int count;
   const int rowid = blockIdx.x;
   const int b = rowid / N, r = rowid % N;
-  const int n = nchunks * kTopK;
-  const uint64_t* src = ws + (int64_t)rowid * n;
-  if (threadIdx.x == 0) {
-    count = 0;
-    thr = 0;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const uint64_t* src = ws + (int64_t)rowid * nlists * kTopK;
+  if (t == 0) count = 0;
+  uint32_t kl = 0;
+  for (int c = t; c < nlists; c += kThreads) {
+    const uint64_t v = src[c * kTopK];
+    cmax[c] = v;
+    const uint32_t k = cand_key(v);
+    kl = k > kl ? k : kl;
   }
-  for (int c = threadIdx.x; c < nchunks; c += kThreads) cmax[c] = src[c * kTopK];
+  const uint32_t tw = wave_kth16<32>(kl);
+  if (lane == 0) wthr[w] = tw;
   __syncthreads();
-  if (nchunks > kTopK) {
-    for (int c = threadIdx.x; c < nchunks; c += kThreads) {
-      uint64_t v = cmax[c];
+  uint32_t Tk = wthr[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) Tk = wthr[i] > Tk ? wthr[i] : Tk;
+  uint64_t T = (uint64_t)Tk << 32;  // the smallest packed word with key Tk
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int c = t; c < nlists; c += kThreads) {
+      if (cmax[c] == 0 || cmax[c] < T) continue;
+      const u32x4_t* l4 = reinterpret_cast<const u32x4_t*>(src + (int64_t)c * kTopK);
+      u32x4_t q[kTopK / 2];
+#pragma unroll
+      for (int i = 0; i < kTopK / 2; ++i) q[i] = l4[i];
+#pragma unroll
+      for (int i = 0; i < kTopK; ++i) {
+        const uint64_t v = ((uint64_t)q[i / 2][2 * (i & 1) + 1] << 32) | q[i / 2][2 * (i & 1)];
+        if (v != 0 && v >= T) {
+          const int pos = atomicAdd(&count, 1);
+          if (pos < kMCap) cand[pos] = v;
+        }
+      }
+    }
+    __syncthreads();
+    if (count <= kMCap || pass == 1) break;
+    // too many ties: the exact 16th largest list maximum
+    if (t == 0) thr = 0;
+    __syncthreads();
+    for (int c = t; c < nlists; c += kThreads) {
+      const uint64_t v = cmax[c];
       int rank = 0;
-      for (int o = 0; o < nchunks; ++o) rank += cmax[o] > v;
+      for (int o = 0; o < nlists; ++o) rank += cmax[o] > v;
       if (rank == kTopK - 1) thr = v;
     }
     __syncthreads();
+    T = thr;
+    if (t == 0) count = 0;
+    __syncthreads();
   }
-  const uint64_t T = thr;
-  for (int i0 = 0; i0 < n; i0 += kThreads * 8) {
-    uint64_t vals[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = i0 + threadIdx.x + kThreads * u;
-      vals[u] = i < n ? src[i] : 0ull;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (vals[u] != 0 && vals[u] >= T) {
-        int pos = atomicAdd(&count, 1);
-        if (pos < kTopK * kTopK) cand[pos] = vals[u];
-      }
-    }
-  }
-  __syncthreads();
-  const int m = count < kTopK * kTopK ? count : kTopK * kTopK;
+  const int m = count < kMCap ? count : kMCap;
   const typename KT::elem_t* row =
       scores + (int64_t)b * seq_stride + (int64_t)(row0 + r) * row_stride;
-  for (int c = threadIdx.x; c < m; c += kThreads) {
-    uint64_t v = cand[c];
+  for (int c = t; c < m; c += kThreads) {
+    const uint64_t v = cand[c];
     int rank = 0;
     for (int o = 0; o < m; ++o) rank += cand[o] > v;
     if (rank < kTopK) {
-      uint32_t x = cand_idx(v);
+      const uint32_t x = cand_idx(v);
       uint32_t u;
       if constexpr (sizeof(typename KT::elem_t) == 2)
         u = reinterpret_cast<const uint16_t*>(row)[x];
@@ -204,52 +416,65 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
 }
 
 struct Plan {
-  int ept;      // elements per thread
-  int vec;      // 16-byte loads
-  int nchunks;
+  int nv;       // 16-byte vectors per lane per wave sub-chunk
+  int vec;      // rows are 16-byte aligned and a whole number of vectors long
+  int seg_len;  // elements per workgroup on average (sizes the grid; a multiple of 4 sub-chunks)
+  int nseg;     // workgroups per row
 };
 
+#ifndef DF2_TOPK_TARGET_WGS
+#define DF2_TOPK_TARGET_WGS 2048
+#endif
+#ifndef DF2_TOPK_NV
+#define DF2_TOPK_NV 0  // 0: chosen by the batch
+#endif
+constexpr int kTargetWGs = DF2_TOPK_TARGET_WGS;
+
 Plan make_plan(int B, int N, int V, int dtype, const void* scores, int64_t seq_stride,
-               int64_t row_stride, int row0) {
+               int64_t row_stride) {
   Plan p;
   const int esz = dtype == DFLASH2_BF16 ? 2 : 4;
+  const int epv = 16 / esz;
   const int64_t rows = (int64_t)B * N;
-  // fewer elements per thread when there are few rows, so that the grid covers the chip
-  int ept = esz == 2 ? 32 : 16;
-  while (ept > 8 && rows * ((V + ept * kThreads - 1) / (ept * kThreads)) < 1024) ept >>= 1;
-  p.ept = ept;
-  p.nchunks = (V + ept * kThreads - 1) / (ept * kThreads);
+  // Small batches (few rows): two vectors per lane per sub-chunk, so a row has fewer,
+  // fuller lists and the merge is short. Larger batches: one, which measured faster on
+  // MI355X (more, smaller copies in flight per compute unit).
+  const int ch1 = kThreads * epv;
+  p.nv = rows * ((V + ch1 - 1) / ch1) < kTargetWGs ? 2 : 1;
+  if (DF2_TOPK_NV) p.nv = DF2_TOPK_NV;
+  const int ch = kThreads * epv * p.nv;
+  const int64_t want = (kTargetWGs + rows - 1) / rows;  // segments per row wanted
+  int64_t seg = (V + want - 1) / want;
+  seg = (seg + ch - 1) / ch * ch;
+  p.seg_len = (int)seg;
+  p.nseg = (int)((V + seg - 1) / seg);
   bool vec = scores == nullptr || aligned(scores, 16);
-  vec = vec && ((seq_stride * esz) % 16 == 0) && ((row_stride * esz) % 16 == 0);
-  (void)row0;
+  vec = vec && ((seq_stride * esz) % 16 == 0) && ((row_stride * esz) % 16 == 0) && V % epv == 0;
   p.vec = vec;
   return p;
-}
-
-template <class KT, int EPT>
-void launch_chunks(const Plan& p, const void* scores, int64_t ss, int64_t rs, int row0, int B,
-                   int N, int V, uint64_t* ws, hipStream_t st) {
-  dim3 grid(p.nchunks, B * N);
-  using E = typename KT::elem_t;
-  if (p.vec)
-    topk_chunk_kernel<KT, EPT, true><<<grid, kThreads, 0, st>>>((const E*)scores, ss, rs, row0, N, V,
-                                                                p.nchunks, ws);
-  else
-    topk_chunk_kernel<KT, EPT, false><<<grid, kThreads, 0, st>>>((const E*)scores, ss, rs, row0, N,
-                                                                 V, p.nchunks, ws);
 }
 
 template <class KT>
 void launch_all(const Plan& p, const void* scores, int64_t ss, int64_t rs, int row0, int B, int N,
                 int V, uint64_t* ws, int32_t* idx, float* val, hipStream_t st) {
-  switch (p.ept) {
-    case 32: launch_chunks<KT, 32>(p, scores, ss, rs, row0, B, N, V, ws, st); break;
-    case 16: launch_chunks<KT, 16>(p, scores, ss, rs, row0, B, N, V, ws, st); break;
-    default: launch_chunks<KT, 8>(p, scores, ss, rs, row0, B, N, V, ws, st); break;
-  }
-  size_t lds = (size_t)p.nchunks * sizeof(uint64_t);
-  topk_merge_kernel<KT><<<B * N, kThreads, lds, st>>>((const typename KT::elem_t*)scores, ss, rs,
-                                                      row0, N, p.nchunks, ws, idx, val);
+  using E = typename KT::elem_t;
+  const dim3 grid(p.nseg, B * N);
+  const E* sc = (const E*)scores;
+  if (!p.vec)
+    topk_wave_scalar_kernel<KT><<<grid, kThreads, 0, st>>>(sc, ss, rs, row0, N, V, p.seg_len,
+                                                           p.nseg, ws);
+  else if (p.nv == 1)
+    topk_wave_kernel<KT, 1, true><<<grid, kThreads, 0, st>>>(sc, ss, rs, row0, N, V, p.seg_len,
+                                                             p.nseg, ws);
+  else if (p.nv == 2)
+    topk_wave_kernel<KT, 2, true><<<grid, kThreads, 0, st>>>(sc, ss, rs, row0, N, V, p.seg_len,
+                                                             p.nseg, ws);
+  else
+    topk_wave_kernel<KT, 4, true><<<grid, kThreads, 0, st>>>(sc, ss, rs, row0, N, V, p.seg_len,
+                                                             p.nseg, ws);
+  const int nlists = p.nseg * kWaves;
+  const size_t lds = (size_t)nlists * sizeof(uint64_t);
+  topk_merge_kernel<KT><<<B * N, kThreads, lds, st>>>(sc, ss, rs, row0, N, nlists, ws, idx, val);
 }
 
 }  // namespace
@@ -259,11 +484,9 @@ using namespace df2;
 
 extern "C" size_t dflash2_topk16_workspace_bytes(int B, int N, int V, int dtype) {
   if (B < 1 || N < 1 || V < kTopK) return 0;
-  Plan p = make_plan(B, N, V, dtype, nullptr, 0, 0, 0);
-  // the plan never picks fewer than 8 elements per thread
-  int64_t nch = (V + 8 * kThreads - 1) / (8 * kThreads);
-  if (p.nchunks > nch) nch = p.nchunks;
-  return round_up((size_t)B * N * nch * kTopK * sizeof(uint64_t), kWsAlign);
+  if (dtype != DFLASH2_BF16 && dtype != DFLASH2_F32) return 0;
+  const Plan p = make_plan(B, N, V, dtype, nullptr, 0, 0);
+  return round_up((size_t)B * N * p.nseg * kWaves * kTopK * sizeof(uint64_t), kWsAlign);
 }
 
 extern "C" int dflash2_topk16(const void* scores, int dtype, int B, int N, int row0,
@@ -276,8 +499,8 @@ extern "C" int dflash2_topk16(const void* scores, int dtype, int B, int N, int r
   if (dtype != DFLASH2_BF16 && dtype != DFLASH2_F32) return DFLASH2_EUNSUPPORTED;
   if (!aligned(ws, kWsAlign) || ws_bytes < dflash2_topk16_workspace_bytes(B, N, V, dtype))
     return DFLASH2_EWORKSPACE;
-  Plan p = make_plan(B, N, V, dtype, scores, seq_stride, row_stride, row0);
-  if ((size_t)p.nchunks * sizeof(uint64_t) > 32 * 1024) return DFLASH2_EUNSUPPORTED;
+  Plan p = make_plan(B, N, V, dtype, scores, seq_stride, row_stride);
+  if ((size_t)p.nseg * kWaves * sizeof(uint64_t) > 32 * 1024) return DFLASH2_EUNSUPPORTED;
   if (dtype == DFLASH2_BF16)
     launch_all<KeyBF16>(p, scores, seq_stride, row_stride, row0, B, N, V, (uint64_t*)ws, idx, val,
                         stream);

@@ -263,7 +263,7 @@ __global__ __launch_bounds__(kThreads) void verify_finish_kernel(
   constexpr int CH = EPT * kThreads;
   const int b = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
   __shared__ uint64_t rowbest[kMaxN + 1];
-  __shared__ uint64_t wsum[kThreads / 64];
+  __shared__ uint64_t wsum[kThreads / 64], wsum2[kThreads / 64];
   __shared__ uint64_t sh_z[2];
   __shared__ int sh_f[kThreads / 64];
   __shared__ int sh_chunk;
@@ -318,39 +318,40 @@ __global__ __launch_bounds__(kThreads) void verify_finish_kernel(
   const ChainRec rec = ws.chain[b];
   st |= rec.flags;
   const float* row = reinterpret_cast<const float*>(tb) + (int64_t)(rec.pos - 1) * row_stride;
+  // thread t owns chunks t*cpt .. t*cpt + cpt - 1 (in index order), so a workgroup scan of
+  // the per-thread sums finds the chunk that holds the draw
+  const int cpt = (nchunks + kThreads - 1) / kThreads;
+  uint64_t my_zr = 0, my_zp = 0;
   {
-    uint64_t zr = 0, zp = 0;
     int f = 0;
-    for (int c = t; c < nchunks; c += kThreads) {
-      zr += ws.zsum[((int64_t)b * nchunks + c) * 2 + 0];
-      zp += ws.zsum[((int64_t)b * nchunks + c) * 2 + 1];
-      f |= ws.zflag[(int64_t)b * nchunks + c];
+    for (int i = 0; i < cpt; ++i) {
+      const int c = t * cpt + i;
+      if (c < nchunks) {
+        my_zr += ws.zsum[((int64_t)b * nchunks + c) * 2 + 0];
+        my_zp += ws.zsum[((int64_t)b * nchunks + c) * 2 + 1];
+        f |= ws.zflag[(int64_t)b * nchunks + c];
+      }
     }
-    zr = wave_sum_u64(zr);
-    zp = wave_sum_u64(zp);
+    const uint64_t zr = wave_sum_u64(my_zr);
+    const uint64_t zp = wave_sum_u64(my_zp);
     f = wave_or(f);
     if (lane == 0) {
       wsum[w] = zr;
+      wsum2[w] = zp;
       sh_f[w] = f;
     }
     __syncthreads();
     if (t == 0) {
-      uint64_t a = 0;
+      uint64_t a = 0, c2 = 0;
       int ff = 0;
       for (int i = 0; i < kThreads / 64; ++i) {
         a += wsum[i];
+        c2 += wsum2[i];
         ff |= sh_f[i];
       }
       sh_z[0] = a;
+      sh_z[1] = c2;
       sh_f[0] = ff;
-    }
-    __syncthreads();
-    if (lane == 0) wsum[w] = zp;
-    __syncthreads();
-    if (t == 0) {
-      uint64_t a = 0;
-      for (int i = 0; i < kThreads / 64; ++i) a += wsum[i];
-      sh_z[1] = a;
     }
     __syncthreads();
   }
@@ -394,19 +395,23 @@ __global__ __launch_bounds__(kThreads) void verify_finish_kernel(
     __syncthreads();
     emitted = sh_tok;
   } else {
-    if (t == 0) {
-      sh_tok = -1;
-      const Draw dr = philox_draw(seed, step, (uint32_t)b, (uint32_t)rec.pos);
-      const uint64_t tau = scale_draw(dr.w[2], Z);
-      uint64_t cum = 0;
-      int c = 0;
-      for (; c < nchunks; ++c) {
+    // every thread draws the same tau; the scan of the per-thread sums finds the chunk
+    const Draw dr = philox_draw(seed, step, (uint32_t)b, (uint32_t)rec.pos);
+    const uint64_t tau_all = scale_draw(dr.w[2], Z);
+    if (t == 0) sh_tok = -1;
+    const uint64_t mine_z = use_resid ? my_zr : my_zp;
+    const uint64_t incl_z = block_incl_scan_u64(mine_z, wsum);
+    const uint64_t excl_z = incl_z - mine_z;
+    if (excl_z <= tau_all && tau_all < incl_z) {
+      uint64_t cum = excl_z;
+      int c = t * cpt;
+      for (int i = 0; i < cpt && c < nchunks; ++i, ++c) {
         const uint64_t zc = ws.zsum[((int64_t)b * nchunks + c) * 2 + (use_resid ? 0 : 1)];
-        if (cum + zc > tau) break;
+        if (cum + zc > tau_all) break;
         cum += zc;
       }
       sh_chunk = c;
-      sh_tau = tau - cum;
+      sh_tau = tau_all - cum;
     }
     __syncthreads();
     // scan the chosen chunk in index order: thread t owns EPT consecutive elements
