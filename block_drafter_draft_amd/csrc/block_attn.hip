@@ -575,22 +575,31 @@ __global__ __launch_bounds__(64 * kStreamWaves) void attn_stream_kernel(
   if (w == 0 && hh == 0) ws_ml[part * kRows + n] = make_float2(M, Lsum);
 }
 
-// Combines the splits of one (sequence, KV head, quarter of D). The (max, sum) pairs of all
-// splits are read in one parallel batch into LDS and turned into weights; then thread (n, c)
-// (query row n, 4 consecutive columns) issues the loads of all its split partials before
-// using any of them.
-template <int D, int MS>
-__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ ws_o,
-                                                           const float2* __restrict__ ws_ml, int P,
-                                                           int Hq, int Hkv, int nsplit,
-                                                           uint16_t* __restrict__ out) {
+// Combines the splits of one (sequence, KV head, slice of CPW columns). Each thread (query
+// row n, 4 columns) issues the loads of all its split partials first; meanwhile the
+// (max, sum) pairs of all splits are read into LDS and turned into weights. Small batches
+// use narrow slices, so that enough workgroups share the reads.
+template <int D, int MS, int CPW>
+__global__ __launch_bounds__(kRows * CPW / 4) void attn_combine_kernel(
+    const float* __restrict__ ws_o, const float2* __restrict__ ws_ml, int P, int Hq, int Hkv,
+    int nsplit, uint16_t* __restrict__ out) {
+  constexpr int TPR = CPW / 4;       // threads per query row
+  constexpr int NT = kRows * TPR;    // threads per workgroup
   __shared__ float wgt[MS][kRows], lsum[MS][kRows];
   __shared__ float inv_den[kRows];
-  const int g = blockIdx.x, b = blockIdx.y, quarter = blockIdx.z;
+  const int g = blockIdx.x, b = blockIdx.y, slice = blockIdx.z;
   const int t = threadIdx.x;
   const int G = Hq / Hkv, rows = P * G;
   const int64_t p0 = ((int64_t)b * Hkv + g) * nsplit;
-  for (int e = t; e < MS * kRows; e += 256) {
+  const int n = t / TPR, c = t % TPR;
+  const int d = slice * CPW + c * 4;
+  float4 v[MS];
+#pragma unroll
+  for (int s = 0; s < MS; ++s) {
+    const int sc = s < nsplit ? s : nsplit - 1;  // in range, so the loads carry no conditions
+    v[s] = *reinterpret_cast<const float4*>(ws_o + ((p0 + sc) * kRows + n) * D + d);
+  }
+  for (int e = t; e < MS * kRows; e += NT) {
     const int s = e / kRows;
     const float2 ml = s < nsplit ? ws_ml[p0 * kRows + e] : make_float2(-INFINITY, 0.0f);
     wgt[s][e % kRows] = ml.x;
@@ -612,15 +621,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
     inv_den[t] = 1.0f / den;
   }
   __syncthreads();
-  const int n = t >> 3, c = t & 7;
-  if (n >= rows || c * 4 >= D / 4) return;  // D/16 threads cover a row's quarter
-  const int d = quarter * (D / 4) + c * 4;
-  float4 v[MS];
-#pragma unroll
-  for (int s = 0; s < MS; ++s) {
-    const int sc = s < nsplit ? s : nsplit - 1;  // in range, so the loads carry no conditions
-    v[s] = *reinterpret_cast<const float4*>(ws_o + ((p0 + sc) * kRows + n) * D + d);
-  }
+  if (n >= rows) return;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int s = 0; s < MS; ++s) {
@@ -638,18 +639,38 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   *reinterpret_cast<uint2*>(dst) = make_uint2(lo2, hi2);
 }
 
-template <int D>
-void launch_combine(const float* ws_o, const float2* ws_ml, int B, int P, int Hq, int Hkv, int nsplit,
-                    uint16_t* out, hipStream_t stream) {
-  const dim3 grid(Hkv, B, 4);
+template <int D, int CPW>
+void launch_combine_w(const float* ws_o, const float2* ws_ml, int B, int P, int Hq, int Hkv,
+                      int nsplit, uint16_t* out, hipStream_t stream) {
+  const dim3 grid(Hkv, B, D / CPW);
+  constexpr int NT = kRows * CPW / 4;
   if (nsplit <= 4)
-    attn_combine_kernel<D, 4><<<grid, 256, 0, stream>>>(ws_o, ws_ml, P, Hq, Hkv, nsplit, out);
+    attn_combine_kernel<D, 4, CPW><<<grid, NT, 0, stream>>>(ws_o, ws_ml, P, Hq, Hkv, nsplit, out);
   else if (nsplit <= 8)
-    attn_combine_kernel<D, 8><<<grid, 256, 0, stream>>>(ws_o, ws_ml, P, Hq, Hkv, nsplit, out);
+    attn_combine_kernel<D, 8, CPW><<<grid, NT, 0, stream>>>(ws_o, ws_ml, P, Hq, Hkv, nsplit, out);
+  else if (nsplit <= 12)
+    attn_combine_kernel<D, 12, CPW><<<grid, NT, 0, stream>>>(ws_o, ws_ml, P, Hq, Hkv, nsplit, out);
   else if (nsplit <= 16)
-    attn_combine_kernel<D, 16><<<grid, 256, 0, stream>>>(ws_o, ws_ml, P, Hq, Hkv, nsplit, out);
+    attn_combine_kernel<D, 16, CPW><<<grid, NT, 0, stream>>>(ws_o, ws_ml, P, Hq, Hkv, nsplit, out);
+  else if (nsplit <= 20)
+    attn_combine_kernel<D, 20, CPW><<<grid, NT, 0, stream>>>(ws_o, ws_ml, P, Hq, Hkv, nsplit, out);
+  else if (nsplit <= 24)
+    attn_combine_kernel<D, 24, CPW><<<grid, NT, 0, stream>>>(ws_o, ws_ml, P, Hq, Hkv, nsplit, out);
   else
-    attn_combine_kernel<D, 32><<<grid, 256, 0, stream>>>(ws_o, ws_ml, P, Hq, Hkv, nsplit, out);
+    attn_combine_kernel<D, 32, CPW><<<grid, NT, 0, stream>>>(ws_o, ws_ml, P, Hq, Hkv, nsplit, out);
+}
+
+template <int D>
+void launch_combine(const float* ws_o, const float2* ws_ml, int B, int P, int Hq, int Hkv,
+                    int nsplit, uint16_t* out, hipStream_t stream) {
+#ifndef DF2_COMBINE_CPW_SMALL
+#define DF2_COMBINE_CPW_SMALL 32
+#endif
+  // small batches may use narrower slices (more workgroups share the reads)
+  if ((int64_t)B * Hkv * (D / 32) < 256)
+    launch_combine_w<D, DF2_COMBINE_CPW_SMALL>(ws_o, ws_ml, B, P, Hq, Hkv, nsplit, out, stream);
+  else
+    launch_combine_w<D, 32>(ws_o, ws_ml, B, P, Hq, Hkv, nsplit, out, stream);
 }
 
 // f32: one wave per query row; lanes hold d and d + 64.

@@ -91,27 +91,41 @@ __global__ __launch_bounds__(256) void select_lattice_kernel(
     }
   }
   __syncthreads();
-  if (kp >= npred) return;
-  const uint16_t* a = A + kp * RS;
   const uint16_t* bb = Bm + k * RS;
   float acc = 0.0f;
   int r = 0;
   if constexpr (VEC) {
+    // fl(A[p,r] g[r]) once per predecessor row, in LDS (it is shared by the 16 successors)
+    float* AG = g + RS;  // [16][RS]
+    for (int e = t; e < npred * (R / 4); e += 256) {
+      const int row = e / (R / 4), c4 = (e % (R / 4)) * 4;
+      const uint2 a4 = *reinterpret_cast<const uint2*>(A + row * RS + c4);
+      const float4 g4 = *reinterpret_cast<const float4*>(g + c4);
+      float4 o;
+      o.x = __fmul_rn(bf16_to_f32(a4.x & 0xffffu), g4.x);
+      o.y = __fmul_rn(bf16_to_f32(a4.x >> 16), g4.y);
+      o.z = __fmul_rn(bf16_to_f32(a4.y & 0xffffu), g4.z);
+      o.w = __fmul_rn(bf16_to_f32(a4.y >> 16), g4.w);
+      *reinterpret_cast<float4*>(AG + row * RS + c4) = o;
+    }
+    __syncthreads();
+    if (kp >= npred) return;
+    const float* ag = AG + kp * RS;
     // eight terms per LDS access, still added one at a time in order
     for (; r < R; r += 8) {
-      const u32x4_t a8 = *reinterpret_cast<const u32x4_t*>(a + r);
       const u32x4_t b8 = *reinterpret_cast<const u32x4_t*>(bb + r);
-      const float4 g0 = *reinterpret_cast<const float4*>(g + r);
-      const float4 g1 = *reinterpret_cast<const float4*>(g + r + 4);
-      const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      const float4 a0 = *reinterpret_cast<const float4*>(ag + r);
+      const float4 a1 = *reinterpret_cast<const float4*>(ag + r + 4);
+      const float aa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float av = bf16_to_f32((a8[e / 2] >> (16 * (e & 1))) & 0xffffu);
         const float bv = bf16_to_f32((b8[e / 2] >> (16 * (e & 1))) & 0xffffu);
-        acc = __fadd_rn(acc, __fmul_rn(__fmul_rn(av, gg[e]), bv));
+        acc = __fadd_rn(acc, __fmul_rn(aa[e], bv));
       }
     }
   } else {
+    if (kp >= npred) return;
+    const uint16_t* a = A + kp * RS;
     for (; r < R; ++r) {
       const float ag = __fmul_rn(bf16_to_f32(a[r]), g[r]);
       const float pr = __fmul_rn(ag, bf16_to_f32(bb[r]));
@@ -135,12 +149,14 @@ __global__ __launch_bounds__(64) void select_path_kernel(
   __shared__ float uni[kMaxN];
   __shared__ int32_t path[kMaxN];
   __shared__ float qout[kMaxN][kTopK];
+  __shared__ int32_t cid[kMaxN * kTopK];
 
-  // index validity (anchor and every candidate)
+  // index validity (anchor and every candidate); the candidates stay in LDS for the end
   int bad = 0;
   if (lane == 0) bad |= !(anchor[b] >= 0 && anchor[b] < V);
   for (int e = lane; e < N * kTopK; e += 64) {
     const int32_t c = cidx[(int64_t)b * N * kTopK + e];
+    cid[e] = c;
     bad |= !(c >= 0 && c < V);
   }
   const bool ok = wave_or(bad) == 0;
@@ -244,16 +260,17 @@ __global__ __launch_bounds__(64) void select_path_kernel(
             break;
           }
         path[i - 1] = pick;
-        for (int k = 0; k < kTopK; ++k) qout[i - 1][k] = __fdiv_rn(e_sh[k], Z);
+        uni[i - 1] = Z;  // this slot's uniform is used; its place now carries Z
       }
       __syncthreads();
+      if (lane < kTopK) qout[i - 1][lane] = __fdiv_rn(e_sh[lane], uni[i - 1]);
       prev = path[i - 1];
     }
     for (int e = lane; e < N * kTopK; e += 64) qq[e] = qout[e / kTopK][e % kTopK];
   }
   if (lane < N) {
     sl[lane] = path[lane];
-    tk[lane] = cidx[((int64_t)b * N + lane) * kTopK + path[lane]];
+    tk[lane] = cid[lane * kTopK + path[lane]];
   }
   if (lane == 0) status[b] = st;
 }
@@ -283,7 +300,9 @@ extern "C" int dflash2_select(const int32_t* cand_idx, const float* cand_val, co
     return DFLASH2_EWORKSPACE;
   float* lattice = (float*)ws;
   const int RS = lat_row_stride(R);
-  const size_t lds = (size_t)2 * kTopK * RS * sizeof(uint16_t) + (size_t)RS * sizeof(float);
+  // predecessor and successor rows (bf16), the gate, and the products fl(A g) (f32)
+  const size_t lds = (size_t)2 * kTopK * RS * sizeof(uint16_t) + (size_t)RS * sizeof(float) +
+                     (size_t)kTopK * RS * sizeof(float);
   const bool vec = R % 8 == 0 && aligned(pred_cb, 16) && aligned(succ_cb, 16) && aligned(gate, 16);
   if (vec)
     select_lattice_kernel<true><<<dim3(N, B), 256, lds, stream>>>(cand_idx, cand_val, gate, pred_cb,
