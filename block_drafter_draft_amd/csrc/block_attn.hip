@@ -423,50 +423,28 @@ __global__ __launch_bounds__(64 * kStreamWaves) void attn_stream_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16_t{};
 
-  auto compute = [&](int tile, int buf) {
+  auto compute = [&](int tile, int buf, bool first) {
     const uint16_t* tk = &sm.kv[w][buf][0][0];
     const uint16_t* tv = &sm.kv[w][buf][1][0];
-    // S^T: accumulator i of lane (n, hh) is tile key 8(i/4) + 4hh + i%4
-    f32x16_t s = f32x16_t{};
+    // S^T: accumulator i of lane (n, hh) is tile key 8(i/4) + 4hh + i%4; two independent
+    // MFMA chains (even and odd k-steps) halve the dependent latency
+    f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
     const int swn = tile_swz(n);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const int c = (2 * ks + hh) ^ swn;
-      const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(tk + n * D + 8 * c);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv), qop[ks], s, 0,
-                                                 0, 0);
+    for (int ks = 0; ks < 8; ks += 2) {
+      const u32x4_t k0 =
+          *reinterpret_cast<const u32x4_t*>(tk + n * D + 8 * ((2 * ks + hh) ^ swn));
+      const u32x4_t k1 =
+          *reinterpret_cast<const u32x4_t*>(tk + n * D + 8 * ((2 * ks + 2 + hh) ^ swn));
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, k0), qop[ks], s0,
+                                                  0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, k1), qop[ks + 1],
+                                                  s1, 0, 0, 0);
     }
-    const int kk0 = tile * kTileKeys;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kk = kk0 + 8 * (i >> 2) + 4 * hh + (i & 3);
-      const bool vis = kk < nctx ? kk >= kmin : kk < nkeys;
-      s[i] = vis ? s[i] * scale_log2 : -INFINITY;
-      mx = fmaxf(mx, s[i]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mnew = fmaxf(m, mx);
-    const float base = mnew == -INFINITY ? 0.0f : mnew;
-    const float alpha = exp2f(m - base);
-    float psum = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      s[i] = exp2f(s[i] - base);
-      psum += s[i];
-    }
-    psum += __shfl_xor(psum, 32, 64);
-    l = l * alpha + psum;
-    m = mnew;
-    bf16x8_t pb[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[u][e] = (__bf16)s[8 * u + e];
     // V^T operand of k-step u, d tile dt: lane (j = lane & 15 of group gq) points at row
     // 16u + 8 iota + 4hh + j/4, columns 32 dt + 16 (gq & 1) + 4 (j & 3) .. +3. The reads are
-    // issued as inline assembly and waited for explicitly: their ordering behind this
-    // tile's copy is already established by the vmcnt wait above.
+    // issued now (inline assembly, waited for explicitly before the PV products), so their
+    // latency overlaps the softmax; this tile's copy has already landed.
     const int gq = lane >> 4, j = lane & 15;
     const uint32_t tv_base = (uint32_t)reinterpret_cast<uintptr_t>(DF2_LDS(tv));
     uint64_t vt[4][2][2];
@@ -483,6 +461,34 @@ __global__ __launch_bounds__(64 * kStreamWaves) void attn_stream_kernel(
           asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(vt[dt][u][io]) : "v"(a));
         }
     }
+    f32x16_t sc = s0 + s1;
+    const int kk0 = tile * kTileKeys;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int kk = kk0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+      const bool vis = kk < nctx ? kk >= kmin : kk < nkeys;
+      sc[i] = vis ? sc[i] * scale_log2 : -INFINITY;
+      mx = fmaxf(mx, sc[i]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mnew = fmaxf(m, mx);
+    const float base = mnew == -INFINITY ? 0.0f : mnew;
+    const float alpha = exp2f(m - base);
+    float psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sc[i] = exp2f(sc[i] - base);
+      psum += sc[i];
+    }
+    psum += __shfl_xor(psum, 32, 64);
+    l = l * alpha + psum;
+    m = mnew;
+    bf16x8_t pb[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[u][e] = (__bf16)sc[8 * u + e];
     asm volatile("s_waitcnt lgkmcnt(0)"
                  : "+v"(vt[0][0][0]), "+v"(vt[0][0][1]), "+v"(vt[0][1][0]), "+v"(vt[0][1][1]),
                    "+v"(vt[1][0][0]), "+v"(vt[1][0][1]), "+v"(vt[1][1][0]), "+v"(vt[1][1][1]),
@@ -490,7 +496,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void attn_stream_kernel(
                    "+v"(vt[3][0][0]), "+v"(vt[3][0][1]), "+v"(vt[3][1][0]), "+v"(vt[3][1][1]));
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      o[dt] *= alpha;
+      if (!first) o[dt] *= alpha;  // on a wave's first tile o is still zero
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const u32x4_t w4 = {(uint32_t)vt[dt][u][0], (uint32_t)(vt[dt][u][0] >> 32),
@@ -510,7 +516,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void attn_stream_kernel(
       asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // tile k + 1's 16 copies may fly on
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    compute(tile, k & 1);
+    compute(tile, k & 1, k == 0);
     if (k + 2 < nmine) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // tile k's LDS reads have returned
       issue(tile + 2 * kStreamWaves, k & 1);
