@@ -15,8 +15,10 @@
 // Candidates are admitted by a threshold key T: every top-16 element of the wave's share
 // has a key >= T. On the first sub-chunk T is the 16th largest lane maximum (at least 16
 // elements reach it), found by a 16- or 32-step bitwise search on ballots; whenever the
-// list grows long it is cut to its 16 best and T rises to the 16th best key, so later
-// sub-chunks admit almost nothing. A sub-chunk holding NaN or an infinity (or overflowing
+// list grows long it is cut to the entries reaching its 16th largest key (found again by a
+// ballot search) and T rises to that key, so later sub-chunks admit almost nothing. Any
+// wave's threshold is valid for the whole row, so the waves of a workgroup share the
+// highest one through LDS. A sub-chunk holding NaN or an infinity (or overflowing
 // the list) is instead reduced exactly, by 16 rounds of a wave maximum of packed words
 // over canonical keys, and its 16 best appended.
 #include "common.hpp"
@@ -41,8 +43,14 @@ __device__ __forceinline__ uint32_t wave_kth16(uint32_t v) {
 }
 
 constexpr int kWaves = kThreads / 64;
-constexpr int kWCap = 256;      // candidate slots per wave
-constexpr int kReduceAt = 64;   // list length that triggers a cut to the best 16
+#ifndef DF2_TOPK_WCAP
+#define DF2_TOPK_WCAP 128
+#endif
+#ifndef DF2_TOPK_REDUCE_AT
+#define DF2_TOPK_REDUCE_AT 64
+#endif
+constexpr int kWCap = DF2_TOPK_WCAP;           // candidate slots per wave
+constexpr int kReduceAt = DF2_TOPK_REDUCE_AT;  // list length that triggers a cut
 constexpr int kBufs = 3;        // LDS buffers per wave (two sub-chunks in flight)
 
 template <class KT, int NV>
@@ -50,6 +58,7 @@ struct WaveSmem {
   u32x4_t buf[kWaves][kBufs][NV][64];  // [wave][buffer][vector][lane]
   uint64_t list[kWaves][kWCap];
   uint64_t top[kWaves][kTopK];
+  uint32_t shared_tf;  // the highest admission threshold any wave has established
 };
 
 template <class KT, int NV, bool VEC>
@@ -65,7 +74,8 @@ __global__ __launch_bounds__(kThreads) void topk_wave_kernel(
   const int seg = blockIdx.x, rowid = blockIdx.y;
   const int b = rowid / N, r = rowid % N;
   const E* row = scores + (int64_t)b * seq_stride + (int64_t)(row0 + r) * row_stride;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   // The row's wave sub-chunks are dealt round-robin: sub-chunk j of wave w of segment seg
   // is the row's sub-chunk (j nseg + seg) 4 + w, so the workgroups of a row move through it
   // side by side.
@@ -81,19 +91,37 @@ __global__ __launch_bounds__(kThreads) void topk_wave_kernel(
   // copy of sub-chunk j into buffer slot: vector v of lane l holds elements
   // wb + v * 64 EPV + l EPV .. + EPV - 1 (wb = the sub-chunk start); rows that are not
   // 16-byte aligned go element by element through registers instead (no copy engine)
+  // past the last sub-chunk: re-read the row's last whole sub-chunk (unused, and the same
+  // for every wave of the row, so it comes from cache)
+  const int wb_dummy = V - WCH > 0 ? V - WCH : 0;
+  const E* lane_row = row + lane * EPV;
   auto issue = [&](int j, int slot) {
-    const int wb = wbase(j);
+    const int wb = j < nsub ? wbase(j) : wb_dummy;  // wave-uniform
+    if (wb + WCH <= V) {
 #pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      int off = wb + v * 64 * EPV + lane * EPV;
-      off = off + EPV <= V ? off : V - EPV;  // past the end: re-read the last vector (unused)
-      __builtin_amdgcn_global_load_lds((const void*)(row + off), DF2_LDS(&sm.buf[w][slot][v][0]),
-                                       16, 0, 0);
+      for (int v = 0; v < NV; ++v)
+        __builtin_amdgcn_global_load_lds((const void*)(lane_row + wb + v * 64 * EPV),
+                                         DF2_LDS(&sm.buf[w][slot][v][0]), 16, 0, 0);
+    } else {
+      // the row's partial last sub-chunk: vectors past the end re-read the last one
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        int off = wb + v * 64 * EPV + lane * EPV;
+        off = off + EPV <= V ? off : V - EPV;
+        __builtin_amdgcn_global_load_lds((const void*)(row + off),
+                                         DF2_LDS(&sm.buf[w][slot][v][0]), 16, 0, 0);
+      }
     }
   };
 
   uint32_t Tf = 0;  // admission threshold on raw keys
   int cnt = 0;      // list length (wave-uniform)
+  // Any wave's threshold is valid for the whole row: at least 16 of the row's elements
+  // reach it. So the waves of a workgroup share the highest one through LDS; a stale read
+  // only means a lower (still valid) threshold.
+  auto publish = [&]() {
+    if (lane == 0) __hip_atomic_fetch_max(&sm.shared_tf, Tf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  };
 
   // cut the list to its best 16; the threshold rises to the 16th key
   auto reduce = [&]() {
@@ -108,8 +136,46 @@ __global__ __launch_bounds__(kThreads) void topk_wave_kernel(
     if (cnt >= kTopK) {
       const uint32_t T = cand_key(list[kTopK - 1]);
       Tf = T == KT::kPosZero ? T - 1 : T;  // -0 ranks equal to +0
+      publish();
     }
     cnt = cnt < kTopK ? cnt : kTopK;
+  };
+
+  // Cheaper cut while streaming: keep the entries whose key reaches the list's 16th largest
+  // key (found by a bitwise search on ballots over all entries; at least 16 are kept, more
+  // only with ties) and raise the threshold to that key. If ties keep the list long, the
+  // exact cut follows.
+  auto shrink = [&]() {
+    uint64_t e[kWCap / 64];
+#pragma unroll
+    for (int i = 0; i < kWCap / 64; ++i) {
+      const int c = lane + 64 * i;
+      e[i] = c < cnt ? list[c] : 0ull;
+    }
+    uint32_t prefix = 0;
+#pragma unroll
+    for (int bit = KB - 1; bit >= 0; --bit) {
+      const uint32_t c = prefix | (1u << bit);
+      int n = 0;
+#pragma unroll
+      for (int i = 0; i < kWCap / 64; ++i) n += __popcll(__ballot(cand_key(e[i]) >= c));
+      if (n >= kTopK) prefix = c;
+    }
+    const uint64_t below = (1ull << lane) - 1;
+    int pos = 0;
+#pragma unroll
+    for (int i = 0; i < kWCap / 64; ++i) {
+      const bool take = e[i] != 0 && cand_key(e[i]) >= prefix;
+      const uint64_t m = __ballot(take);
+      if (take) list[pos + __popcll(m & below)] = e[i];
+      pos += __popcll(m);
+    }
+    cnt = pos;
+    if (prefix > 0) {
+      Tf = prefix == KT::kPosZero ? prefix - 1 : prefix;  // -0 ranks equal to +0
+      publish();
+    }
+    if (cnt > kReduceAt / 2) reduce();
   };
 
   // any sub-chunk, element by element (partial sub-chunks, f32 rows)
@@ -133,6 +199,7 @@ __global__ __launch_bounds__(kThreads) void topk_wave_kernel(
     if (j == 0) {
       const uint32_t T = wave_kth16<KB>(kmax);
       Tf = T == KT::kPosZero ? T - 1 : T;
+      publish();
     }
     const int cnt0 = cnt;
     if (!any_special) {
@@ -173,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void topk_wave_kernel(
       cnt = cnt0 + kTopK;
       reduce();
     } else if (cnt > kReduceAt) {
-      reduce();
+      shrink();
     }
   };
 
@@ -192,8 +259,10 @@ __global__ __launch_bounds__(kThreads) void topk_wave_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t u = q[v][i];
-        const uint32_t sgn = (u >> 15) & 0x00010001u;
-        const uint32_t k2 = u ^ (0x80008000u | (sgn * 0x7fffu));
+        typedef short i16x2_t __attribute__((ext_vector_type(2)));
+        // per half: 0xffff if negative, else 0 (packed arithmetic shift)
+        const uint32_t neg = __builtin_bit_cast(uint32_t, __builtin_bit_cast(i16x2_t, u) >> 15);
+        const uint32_t k2 = u ^ (0x80008000u | neg);
         key2[4 * v + i] = k2;
         const u16x2_t kk = __builtin_bit_cast(u16x2_t, k2);
         mx2 = __builtin_elementwise_max(mx2, kk);
@@ -205,6 +274,7 @@ __global__ __launch_bounds__(kThreads) void topk_wave_kernel(
     if (j == 0) {
       const uint32_t T = wave_kth16<KB>(kmax);
       Tf = T == KT::kPosZero ? T - 1 : T;
+      publish();
     }
     if (__ballot(kmax >= Tf) == 0) return true;
     const int cnt0_fast = cnt;
@@ -227,16 +297,22 @@ __global__ __launch_bounds__(kThreads) void topk_wave_kernel(
       cnt = cnt0_fast;  // the kept list is intact below cnt0_fast
       return false;
     }
-    if (cnt > kReduceAt) reduce();
+    if (cnt > kReduceAt) shrink();
     return true;
   };
 
   // three buffers: sub-chunks j + 1 and j + 2 are in flight while j is examined. Every
   // iteration issues exactly NV copies (clamped past the end), so "all but the newest
   // 2 NV copies have landed" means sub-chunk j is in LDS.
+  if (threadIdx.x == 0) sm.shared_tf = 0;
+  __syncthreads();
   issue(0, 0);
   issue(1, 1);
   for (int j = 0; j < nsub; ++j) {
+    if (j > 0) {
+      const uint32_t st = __hip_atomic_load(&sm.shared_tf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      Tf = st > Tf ? st : Tf;
+    }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // sub-chunk j - 1's reads are done
     issue(j + 2, (j + 2) % kBufs);
     if constexpr (NV == 1)
@@ -436,12 +512,8 @@ Plan make_plan(int B, int N, int V, int dtype, const void* scores, int64_t seq_s
   const int esz = dtype == DFLASH2_BF16 ? 2 : 4;
   const int epv = 16 / esz;
   const int64_t rows = (int64_t)B * N;
-  // Small batches (few rows): two vectors per lane per sub-chunk, so a row has fewer,
-  // fuller lists and the merge is short. Larger batches: one, which measured faster on
-  // MI355X (more, smaller copies in flight per compute unit).
-  const int ch1 = kThreads * epv;
-  p.nv = rows * ((V + ch1 - 1) / ch1) < kTargetWGs ? 2 : 1;
-  if (DF2_TOPK_NV) p.nv = DF2_TOPK_NV;
+  // two 16-byte vectors per lane per sub-chunk (measured best on MI355X at batch 1 and 64)
+  p.nv = DF2_TOPK_NV ? DF2_TOPK_NV : 2;
   const int ch = kThreads * epv * p.nv;
   const int64_t want = (kTargetWGs + rows - 1) / rows;  // segments per row wanted
   int64_t seg = (V + want - 1) / want;
