@@ -153,3 +153,46 @@ def test_topk16_deterministic(d2):
     b = run_gpu(d2, draft, 1, 7, 1, 8 * cfg.V, cfg.V, cfg.V)
     np.testing.assert_array_equal(a[0], b[0])
     np.testing.assert_array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+
+
+def _bf16(x):
+    return wl.to_bf16_bits(np.asarray(x, np.float32))
+
+
+@pytest.mark.parametrize("case", ["late_specials", "tie_plateau", "rising", "unaligned_long",
+                                  "f32_late_specials"])
+def test_topk16_long_rows_adversarial(d2, case):
+    # Full-width rows whose decisive elements sit deep in the row, so that they meet the
+    # running thresholds of many sub-chunks and workgroups: NaN (both signs, quiet and
+    # signalling patterns) and infinities placed late, a plateau of equal maxima spread over
+    # the whole row, values that rise along the row (every sub-chunk raises the threshold),
+    # and a row length that is not a whole number of 16-byte vectors (the register-load path).
+    seed = {"late_specials": 61, "tie_plateau": 62, "rising": 63, "unaligned_long": 64,
+            "f32_late_specials": 65}[case]
+    rng = np.random.default_rng(seed)
+    V = 248317 if case == "unaligned_long" else 248320
+    B, N = 8, 7
+    x = rng.standard_normal((B, N + 1, V)).astype(np.float32) * 2.0
+    if case == "tie_plateau":
+        x = np.round(x)                            # few distinct values
+        for b in range(B):
+            for r in range(1, N + 1):
+                pos = rng.choice(V, size=40, replace=False)
+                x[b, r, pos] = 9.0                 # 40 equal maxima, ties by index
+    elif case == "rising":
+        x += np.linspace(0.0, 30.0, V, dtype=np.float32)[None, None, :]
+    f32 = case.startswith("f32")
+    host = x if f32 else _bf16(x)
+    if case.endswith("late_specials"):
+        if f32:
+            pats = [0x7FC00000, 0xFFC00000, 0x7F800001, 0x7F800000, 0xFF800000, 0x80000000]
+            bits = host.view(np.uint32)
+        else:
+            pats = [0x7FC0, 0xFFC0, 0x7F81, 0x7F80, 0xFF80, 0x8000]
+            bits = host
+        for b in range(B):
+            for r in range(1, N + 1):
+                pos = rng.choice(np.arange(V // 2, V), size=len(pats), replace=False)
+                for p_, v_ in zip(pos, pats):
+                    bits[b, r, p_] = v_
+    check(d2, host, B, N, 1, (N + 1) * V, V, V, f"long rows {case}")
