@@ -321,38 +321,39 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
 // hands each lane four keys of one column. Rows land in LDS with their 16-byte chunks
 // XOR-swizzled by the row index, so that both the K reads (16 rows, one chunk) and the
 // transposed V reads (4 rows, 4 chunks per half-wave) hit distinct banks. At the end the
-// four waves' states are merged through LDS, each wave producing a quarter of the columns.
+// waves' states are merged through LDS, each wave producing its share of the columns.
+// NW (waves per workgroup) is 4 when the grid is about one workgroup per compute unit
+// (128 KiB of tile buffers each), and 2 for large batches, so that two workgroups share a
+// unit and the whole grid is resident in one round.
 constexpr int kTileKeys = 32;
-#ifndef DF2_STREAM_WAVES
-#define DF2_STREAM_WAVES 4
-#endif
-constexpr int kStreamWaves = DF2_STREAM_WAVES;  // waves per workgroup
 constexpr int kStreamD = 128;
 constexpr int kTileElems = kTileKeys * kStreamD;     // one tensor's tile (8 KiB of bf16)
 constexpr int kMergeStride = 40;                      // floats per d row of a merge state
 
 #define DF2_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
+template <int NW>
 struct StreamSmem {
   union {
-    uint16_t kv[kStreamWaves][2][2][kTileElems];           // [wave][buffer][K, V][tile]
-    float o[kStreamWaves][kStreamD][kMergeStride];         // [wave][d][query row]
+    uint16_t kv[NW][2][2][kTileElems];           // [wave][buffer][K, V][tile]
+    float o[NW][kStreamD][kMergeStride];         // [wave][d][query row]
   };
-  float m[kStreamWaves][kRows], l[kStreamWaves][kRows];
+  float m[NW][kRows], l[NW][kRows];
 };
 
 // chunk swizzle of tile row r: 16 consecutive rows get 16 distinct values, and 4
 // consecutive rows (aligned to 4) land in 4 different groups of four chunks
 __device__ __forceinline__ int tile_swz(int r) { return ((r & 3) << 2) ^ ((r >> 2) & 3); }
 
-__global__ __launch_bounds__(64 * kStreamWaves) void attn_stream_kernel(
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void attn_stream_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kb,
     const uint16_t* __restrict__ vb, const uint16_t* __restrict__ kr,
     const uint16_t* __restrict__ vr, const int32_t* __restrict__ ctx_len, int P, int Hq, int Hkv,
     int S, int W, float scale_log2, int nsplit, int tiles_per_split, float* __restrict__ ws_o,
     float2* __restrict__ ws_ml, uint16_t* __restrict__ out) {
   constexpr int D = kStreamD;
-  __shared__ StreamSmem sm;
+  __shared__ StreamSmem<NW> sm;
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int t = threadIdx.x, w = t >> 6, lane = t & 63, n = lane & 31, hh = lane >> 5;
   const int G = Hq / Hkv, rows = P * G;
@@ -365,8 +366,8 @@ __global__ __launch_bounds__(64 * kStreamWaves) void attn_stream_kernel(
   const int tbeg = split * tiles_per_split;
   int tend = tbeg + tiles_per_split;
   tend = tend < ntiles ? tend : ntiles;
-  // this wave's tiles: tbeg + w, tbeg + w + 4, ...
-  const int nmine = tend - tbeg - w > 0 ? (tend - tbeg - w + kStreamWaves - 1) / kStreamWaves : 0;
+  // this wave's tiles: tbeg + w, tbeg + w + NW, ...
+  const int nmine = tend - tbeg - w > 0 ? (tend - tbeg - w + NW - 1) / NW : 0;
 
   // Q^T as the B operand: lane (n, hh) holds q[n][16 ks + 8 hh .. +7]
   const bool qvalid = n < rows;
@@ -509,9 +510,9 @@ __global__ __launch_bounds__(64 * kStreamWaves) void attn_stream_kernel(
 
   // two tiles in flight from the start; tile k + 2 reuses tile k's buffer once it is read
   if (nmine > 0) issue(tbeg + w, 0);
-  if (nmine > 1) issue(tbeg + w + kStreamWaves, 1);
+  if (nmine > 1) issue(tbeg + w + NW, 1);
   for (int k = 0; k < nmine; ++k) {
-    const int tile = tbeg + w + kStreamWaves * k;
+    const int tile = tbeg + w + NW * k;
     if (k + 1 < nmine)
       asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // tile k + 1's 16 copies may fly on
     else
@@ -519,7 +520,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void attn_stream_kernel(
     compute(tile, k & 1, k == 0);
     if (k + 2 < nmine) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // tile k's LDS reads have returned
-      issue(tile + 2 * kStreamWaves, k & 1);
+      issue(tile + 2 * NW, k & 1);
     }
   }
 
@@ -537,27 +538,27 @@ __global__ __launch_bounds__(64 * kStreamWaves) void attn_stream_kernel(
     sm.l[w][n] = l;
   }
   __syncthreads();
-  float mw[kStreamWaves], M = -INFINITY;
+  float mw[NW], M = -INFINITY;
 #pragma unroll
-  for (int v = 0; v < kStreamWaves; ++v) {
+  for (int v = 0; v < NW; ++v) {
     mw[v] = sm.m[v][n];
     M = fmaxf(M, mw[v]);
   }
-  float aw[kStreamWaves], Lsum = 0.0f;
+  float aw[NW], Lsum = 0.0f;
 #pragma unroll
-  for (int v = 0; v < kStreamWaves; ++v) {
+  for (int v = 0; v < NW; ++v) {
     aw[v] = M == -INFINITY ? 0.0f : exp2f(mw[v] - M);
     Lsum += aw[v] * sm.l[v][n];
   }
   // lane (n, hh): query row n, CPL columns from d0
-  constexpr int CPL = D / kStreamWaves / 2;
-  const int d0 = (D / kStreamWaves) * w + CPL * hh;
+  constexpr int CPL = D / NW / 2;
+  const int d0 = (D / NW) * w + CPL * hh;
   float acc[CPL];
 #pragma unroll
   for (int e = 0; e < CPL; ++e) {
     float a = 0.0f;
 #pragma unroll
-    for (int v = 0; v < kStreamWaves; ++v) a += aw[v] * sm.o[v][d0 + e][n];
+    for (int v = 0; v < NW; ++v) a += aw[v] * sm.o[v][d0 + e][n];
     acc[e] = a;
   }
   if (nsplit == 1) {
@@ -728,6 +729,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(
 struct SplitPlan {
   int nsplit;
   int stages_per_split;
+  int nw;  // waves per workgroup (streaming kernel)
 };
 
 // Enough workgroups to cover the chip at small batch, one split per (sequence, KV head)
@@ -744,29 +746,34 @@ SplitPlan plan_splits(int B, int Hkv, int W) {
   p.stages_per_split = p.stages_per_split < 1 ? 1 : p.stages_per_split;
   p.nsplit = (stages + p.stages_per_split - 1) / p.stages_per_split;
   p.nsplit = p.nsplit < 1 ? 1 : p.nsplit;
+  p.nw = 4;
   return p;
 }
 
-// D = 128 streaming kernel: each workgroup should have at least kStreamMinTiles tiles
-// (one per wave), and a launch about kStreamTargetWGs workgroups (one per compute unit,
-// the LDS buffers allowing one workgroup per unit).
+// D = 128 streaming kernel. Up to one (sequence, KV head) per compute unit, workgroups of
+// four waves, split so that a launch has about kStreamTargetWGs workgroups (one per unit:
+// the tile buffers allow one such workgroup per unit) with at least one tile per wave.
+// Beyond that, workgroups of two waves, two per unit, one per (sequence, KV head).
 #ifndef DF2_STREAM_TARGET_WGS
 #define DF2_STREAM_TARGET_WGS 256
 #endif
-#ifndef DF2_STREAM_MIN_TILES
-#define DF2_STREAM_MIN_TILES 4
+#ifndef DF2_STREAM_NW
+#define DF2_STREAM_NW 0  // 0: by the batch
 #endif
+constexpr int kComputeUnits = 256;
 SplitPlan plan_stream(int B, int Hkv, int P, int W) {
   const int ntiles = (W - 1 + P + kTileKeys - 1) / kTileKeys;  // tiles of the longest list
   const int units = B * Hkv;
+  const int nw = DF2_STREAM_NW ? DF2_STREAM_NW : (units > kComputeUnits ? 2 : 4);
   int ns = (DF2_STREAM_TARGET_WGS + units - 1) / units;
-  const int by_tiles = (ntiles + DF2_STREAM_MIN_TILES - 1) / DF2_STREAM_MIN_TILES;
+  const int by_tiles = (ntiles + nw - 1) / nw;
   ns = ns < by_tiles ? ns : by_tiles;
   ns = ns < kMaxSplits ? ns : kMaxSplits;
   ns = ns < 1 ? 1 : ns;
   SplitPlan p;
   p.stages_per_split = (ntiles + ns - 1) / ns;  // tiles per split
   p.nsplit = (ntiles + p.stages_per_split - 1) / p.stages_per_split;
+  p.nw = nw;
   return p;
 }
 
@@ -826,10 +833,16 @@ extern "C" int dflash2_block_attn(const void* q, const void* k_blk, const void* 
   const float sl2 = scale * kLog2e;
   dim3 grid(sp.nsplit, Hkv, B);
   if (D == 128) {
-    attn_stream_kernel<<<grid, 64 * kStreamWaves, 0, stream>>>(
-        (const uint16_t*)q, (const uint16_t*)k_blk, (const uint16_t*)v_blk,
-        (const uint16_t*)k_ring, (const uint16_t*)v_ring, ctx_len, P, Hq, Hkv, S, W, sl2,
-        sp.nsplit, sp.stages_per_split, ws_o, ws_ml, (uint16_t*)out);
+    if (sp.nw == 2)
+      attn_stream_kernel<2><<<grid, 128, 0, stream>>>(
+          (const uint16_t*)q, (const uint16_t*)k_blk, (const uint16_t*)v_blk,
+          (const uint16_t*)k_ring, (const uint16_t*)v_ring, ctx_len, P, Hq, Hkv, S, W, sl2,
+          sp.nsplit, sp.stages_per_split, ws_o, ws_ml, (uint16_t*)out);
+    else
+      attn_stream_kernel<4><<<grid, 256, 0, stream>>>(
+          (const uint16_t*)q, (const uint16_t*)k_blk, (const uint16_t*)v_blk,
+          (const uint16_t*)k_ring, (const uint16_t*)v_ring, ctx_len, P, Hq, Hkv, S, W, sl2,
+          sp.nsplit, sp.stages_per_split, ws_o, ws_ml, (uint16_t*)out);
     if (sp.nsplit > 1) launch_combine<128>(ws_o, ws_ml, B, P, Hq, Hkv, sp.nsplit, (uint16_t*)out, stream);
   } else {
     attn_split_kernel<64><<<grid, 256, 0, stream>>>(

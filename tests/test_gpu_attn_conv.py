@@ -80,6 +80,18 @@ def test_attn_shapes(d2, P, Hq, Hkv, D, S, W):
     run_attn(d2, q, kb, vb, kr, vr, L, W, f"shape P{P} Hq{Hq} Hkv{Hkv} D{D} S{S} W{W}")
 
 
+@pytest.mark.parametrize("B,P,Hq,Hkv,S,W", [(36, 8, 32, 8, 2048, 2048), (20, 5, 32, 16, 700, 600)])
+def test_attn_large_batch_two_wave_workgroups(d2, B, P, Hq, Hkv, S, W):
+    # more (sequence, KV head) pairs than compute units: the streaming kernel runs
+    # workgroups of two waves, two per unit; contexts cover empty, short, ragged-tile,
+    # wrapped-ring and full windows
+    rng = np.random.default_rng(B * 17 + Hkv)
+    base = [0, 1, 9, 31, 33, W - 2, W - 1, W, W + 5, 3 * S + 7, 131071]
+    L = [base[i % len(base)] for i in range(B)]
+    q, kb, vb, kr, vr = _rand_attn(rng, B, P, Hq, Hkv, 128, S)
+    run_attn(d2, q, kb, vb, kr, vr, L, W, f"two-wave workgroups B{B} Hkv{Hkv}")
+
+
 def test_attn_f32_shapes(d2):
     rng = np.random.default_rng(52)
     L = [0, 10, 100]
