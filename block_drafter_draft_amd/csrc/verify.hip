@@ -3,8 +3,9 @@
 // proposals, greedy keeps the deterministic chain; drafter-geometry paragraph: the target
 // consumes the anchor plus all proposals, so an all-accept step has a bonus row).
 //
-// Kernel 1 (grid: chunks x sequences) reads each needed target row chunk once:
-//   greedy  - rows 0..N: the chunk's first element under the top-16 order (packed word);
+// Kernel 1 (grid: chunks x row groups x sequences) reads each needed target row chunk once:
+//   greedy  - rows 0..N: the chunk's first element under the top-16 order (packed word),
+//             a group of rows per workgroup;
 //   sampled - the accept chain is cheap (N gathers and N Philox draws, one per lane), so
 //             every workgroup of the sequence recomputes it and then reads only the row it
 //             will draw from: the chunk sums of the integer weights floor(w * 2^40), both
@@ -64,23 +65,22 @@ __device__ __forceinline__ uint32_t load_bits(const typename KT::elem_t* p, int6
 
 // Accept chain of a sampled sequence, computed by wave 0 (lane j-1 tests proposal j) and
 // published in *rec (LDS). All threads must call; returns after a barrier.
+// x and sl are lane t's proposal token and slot (loaded by the caller; t < N).
 __device__ void accept_chain(const float* __restrict__ tgt, int64_t row_stride, int V, int N,
-                             const int32_t* __restrict__ tokens, const int32_t* __restrict__ cidx,
-                             const float* __restrict__ q, const int32_t* __restrict__ slot,
-                             uint64_t seed, uint64_t step, int b, ChainRec* rec) {
+                             int32_t x, int32_t sl, const int32_t* __restrict__ cidx,
+                             const float* __restrict__ q, uint64_t seed, uint64_t step, int b,
+                             ChainRec* rec) {
   const int t = threadIdx.x;
   if (t < 64) {
     bool acc = false, plain = false;
     int fl = 0;
     if (t < N) {
       const int j = t + 1;
-      const int32_t x = tokens[(int64_t)b * N + t];
       Draw d = philox_draw(seed, step, (uint32_t)b, (uint32_t)j);
       const float u = uniform24(d.w[1]);
       if (x < 0 || x >= V) {
         plain = true;
       } else {
-        const int32_t sl = slot[(int64_t)b * N + t];
         const int32_t* ci = cidx + ((int64_t)b * N + t) * kTopK;
         if (sl < 0 || sl >= kTopK || ci[sl] != x) {
           fl |= DFLASH2_ST_BADTOKEN;
@@ -107,7 +107,64 @@ __device__ void accept_chain(const float* __restrict__ tgt, int64_t row_stride, 
   __syncthreads();
 }
 
+// The first element of one row chunk under the top-16 order (packed key and index), over
+// the whole workgroup's wave: exact for any contents. Elements at or past V do not count.
 template <class KT, int EPT, bool VEC>
+__device__ __forceinline__ uint64_t chunk_best_exact(const uint32_t (&bits)[EPT], int base, int V) {
+  uint32_t bk = 0, bi = 0;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int x = index_of<EPT, VEC, KT>(base, e);
+    const uint32_t k = x < V ? KT::canon(bits[e]) : 0u;
+    if (k > bk) {
+      bk = k;
+      bi = (uint32_t)x;
+    }
+  }
+  return wave_max_u64(bk ? pack_cand(bk, bi) : 0ull);
+}
+
+// The same for a chunk that lies wholly inside the row (16-byte loads). Keys are the plain
+// sign-magnitude flip; that is the canonical key unless an element is a NaN, or a signed
+// zero is a lane's largest key. A wave that sees either goes the exact way; otherwise the
+// wave maximum M is found with one 32-bit reduction and its first holder in index order
+// by ballots (element e of vector v of lane l sits at v*256*EPV + (64*wave + l)*EPV + e).
+template <class KT, int EPT>
+__device__ __forceinline__ uint64_t chunk_best_full(const uint32_t (&bits)[EPT], int base, int V) {
+  constexpr int EPV = ChunkLoad<KT, EPT>::kEPV;
+  constexpr int NV = EPT / EPV;
+  uint32_t k[EPT];
+  uint32_t mx = 0u, mn = 0xffffffffu;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    k[e] = KT::raw(bits[e]);
+    mx = k[e] > mx ? k[e] : mx;
+    mn = k[e] < mn ? k[e] : mn;
+  }
+  const bool special = mx > KT::kPosInf || mn < KT::kNegInf || mx == KT::kNegZeroRaw ||
+                       mx == KT::kPosZero;
+  if (__ballot(special)) return chunk_best_exact<KT, EPT, true>(bits, base, V);
+  const uint32_t M = wave_max_u32(mx);
+  const int wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    int ef = EPV;
+#pragma unroll
+    for (int e = EPV - 1; e >= 0; --e) ef = k[v * EPV + e] == M ? e : ef;
+    const uint64_t holders = __ballot(ef < EPV);
+    if (holders) {
+      const int L = __ffsll((unsigned long long)holders) - 1;
+      const int e = __shfl(ef, L, 64);
+      const int x = base + v * (kChunkThreads * EPV) + (64 * wv + L) * EPV + e;
+      return pack_cand(M, (uint32_t)x);
+    }
+  }
+  return 0ull;  // not reached: some lane holds M
+}
+
+// Grid: (chunks, row groups, sequences). A greedy sequence's workgroup takes RG rows of
+// one chunk; a sampled sequence uses row group 0 only.
+template <class KT, int EPT, bool VEC, int RG>
 __global__ __launch_bounds__(kThreads) void verify_rows_kernel(
     const typename KT::elem_t* __restrict__ target, int64_t seq_stride, int64_t row_stride, int V,
     const int32_t* __restrict__ tokens, const int32_t* __restrict__ cidx,
@@ -115,13 +172,18 @@ __global__ __launch_bounds__(kThreads) void verify_rows_kernel(
     const float* __restrict__ temperature, uint64_t seed, uint64_t step, int N, int nchunks,
     Ws ws) {
   constexpr int CH = EPT * kThreads;
-  constexpr int kRowGroup = 8;  // rows whose loads are issued together
-  const int chunk = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  const int chunk = blockIdx.x, grp = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
   const int base = chunk * CH;
   __shared__ ChainRec rec;
-  __shared__ uint64_t red[kThreads / 64][kRowGroup];
+  __shared__ uint64_t red[kThreads / 64][RG < 2 ? 2 : RG];  // the sampled path uses two
   __shared__ int redf[kThreads / 64];
 
+  // a sampled chain's first loads do not depend on the temperature: issue them with it
+  int32_t x_pre = -1, sl_pre = -1;
+  if (t < N) {
+    x_pre = tokens[(int64_t)b * N + t];
+    sl_pre = slot[(int64_t)b * N + t];
+  }
   int st = 0;
   float invT = 0.0f;
   int mode = temp_mode(temperature[b], &invT, &st);
@@ -130,56 +192,46 @@ __global__ __launch_bounds__(kThreads) void verify_rows_kernel(
   const typename KT::elem_t* tb = target + (int64_t)b * seq_stride;
 
   if (mode == 0) {
-    // greedy: the chunk maximum of every row, eight rows per round of loads
-    for (int r0 = 0; r0 <= N; r0 += kRowGroup) {
-      uint32_t bits[kRowGroup][EPT];
-      // rows past N re-read row N (ignored below), so the loads carry no conditions
-      if (VEC && base + CH <= V) {
+    // greedy: the chunk's first element of rows r0 .. r0 + RG - 1, all loads issued together
+    const int r0 = grp * RG;
+    if (r0 > N) return;
+    uint32_t bits[RG][EPT];
+    const bool full = VEC && base + CH <= V;
+    // rows past N re-read row N (ignored below), so the loads carry no conditions
+    if (full) {
 #pragma unroll
-        for (int rr = 0; rr < kRowGroup; ++rr) {
-          const int r = r0 + rr <= N ? r0 + rr : N;
-          load_chunk_full<KT, EPT>(tb + (int64_t)r * row_stride, base, bits[rr]);
-        }
-      } else {
-#pragma unroll
-        for (int rr = 0; rr < kRowGroup; ++rr) {
-          const int r = r0 + rr <= N ? r0 + rr : N;
-          load_chunk<KT, EPT, VEC>(tb + (int64_t)r * row_stride, base, V, bits[rr]);
-        }
+      for (int rr = 0; rr < RG; ++rr) {
+        const int r = r0 + rr <= N ? r0 + rr : N;
+        load_chunk_full<KT, EPT>(tb + (int64_t)r * row_stride, base, bits[rr]);
       }
+    } else {
 #pragma unroll
-      for (int rr = 0; rr < kRowGroup; ++rr) {
-        uint64_t m = 0;
-        if (r0 + rr <= N) {
-          uint32_t bk = 0, bi = 0;
+      for (int rr = 0; rr < RG; ++rr) {
+        const int r = r0 + rr <= N ? r0 + rr : N;
+        load_chunk<KT, EPT, VEC>(tb + (int64_t)r * row_stride, base, V, bits[rr]);
+      }
+    }
 #pragma unroll
-          for (int e = 0; e < EPT; ++e) {
-            const int x = index_of<EPT, VEC, KT>(base, e);
-            const uint32_t k = x < V ? KT::canon(bits[rr][e]) : 0u;
-            if (k > bk) {
-              bk = k;
-              bi = (uint32_t)x;
-            }
-          }
-          m = bk ? pack_cand(bk, bi) : 0ull;
-        }
-        m = wave_max_u64(m);
-        if ((t & 63) == 0) red[t >> 6][rr] = m;
-      }
-      __syncthreads();
-      if (t < kRowGroup && r0 + t <= N) {
-        uint64_t g = red[0][t];
-        for (int w = 1; w < kThreads / 64; ++w) g = red[w][t] > g ? red[w][t] : g;
-        ws.best[((int64_t)b * (N + 1) + r0 + t) * nchunks + chunk] = g;
-      }
-      __syncthreads();
+    for (int rr = 0; rr < RG; ++rr) {
+      uint64_t m = 0;
+      if (r0 + rr <= N)
+        m = full ? chunk_best_full<KT, EPT>(bits[rr], base, V)
+                 : chunk_best_exact<KT, EPT, VEC>(bits[rr], base, V);
+      if ((t & 63) == 0) red[t >> 6][rr] = m;
+    }
+    __syncthreads();
+    if (t < RG && r0 + t <= N) {
+      uint64_t g = red[0][t];
+      for (int w = 1; w < kThreads / 64; ++w) g = red[w][t] > g ? red[w][t] : g;
+      ws.best[((int64_t)b * (N + 1) + r0 + t) * nchunks + chunk] = g;
     }
     return;
   }
+  if (grp != 0) return;
 
   // sampled: which row, and with which candidate corrections
   const float* tgt = reinterpret_cast<const float*>(tb);
-  accept_chain(tgt, row_stride, V, N, tokens, cidx, q, slot, seed, step, b, &rec);
+  accept_chain(tgt, row_stride, V, N, x_pre, sl_pre, cidx, q, seed, step, b, &rec);
   if (chunk == 0 && t == 0) ws.chain[b] = rec;
   const float* row = tgt + (int64_t)(rec.pos - 1) * row_stride;
 
@@ -468,11 +520,23 @@ constexpr int kEPT = 8;  // elements per thread: one 16-byte bf16 vector or two 
 struct Plan {
   int nchunks;
   bool vec;
+  int rg;  // rows per greedy workgroup: 1, 2 or 4 (8 with DF2_VERIFY_RG)
 };
 
-Plan make_plan(int V, int dtype, const void* target, int64_t ss, int64_t rs) {
+// Rows per greedy workgroup: four (measured best at batch 16 and 64: fewer registers than
+// eight, so more workgroups in flight), fewer while the grid would have under about 1024
+// workgroups (batch 1 takes one row per workgroup).
+#ifndef DF2_VERIFY_RG
+#define DF2_VERIFY_RG 0  // 0: by the batch
+#endif
+constexpr int kVerifyTargetWGs = 1024;
+
+Plan make_plan(int B, int N, int V, int dtype, const void* target, int64_t ss, int64_t rs) {
   Plan p;
   p.nchunks = (V + kEPT * kThreads - 1) / (kEPT * kThreads);
+  int rg = 4;
+  while (rg > 1 && (int64_t)B * p.nchunks * ((N + 1 + rg - 1) / rg) < kVerifyTargetWGs) rg >>= 1;
+  p.rg = DF2_VERIFY_RG ? DF2_VERIFY_RG : rg;
   const int esz = dtype == DFLASH2_BF16 ? 2 : 4;
   p.vec = (target == nullptr || aligned(target, 16)) && (ss * esz) % 16 == 0 && (rs * esz) % 16 == 0;
   return p;
@@ -484,8 +548,17 @@ void launch(const Plan& p, const void* target, int64_t ss, int64_t rs, int V,
             const float* temp, uint64_t seed, uint64_t step, int B, int N, Ws w, int32_t* n_acc,
             int32_t* out, int32_t* status, hipStream_t st) {
   using E = typename KT::elem_t;
-  verify_rows_kernel<KT, kEPT, VEC><<<dim3(p.nchunks, B), kThreads, 0, st>>>(
-      (const E*)target, ss, rs, V, tokens, cidx, q, slot, temp, seed, step, N, p.nchunks, w);
+  const dim3 grid(p.nchunks, (N + 1 + p.rg - 1) / p.rg, B);
+#define DF2_ROWS(RG)                                                                     \
+  verify_rows_kernel<KT, kEPT, VEC, RG><<<grid, kThreads, 0, st>>>(                      \
+      (const E*)target, ss, rs, V, tokens, cidx, q, slot, temp, seed, step, N, p.nchunks, w)
+  switch (p.rg) {
+    case 1: DF2_ROWS(1); break;
+    case 2: DF2_ROWS(2); break;
+    case 4: DF2_ROWS(4); break;
+    default: DF2_ROWS(8); break;
+  }
+#undef DF2_ROWS
   verify_finish_kernel<KT, kEPT><<<B, kThreads, 0, st>>>((const E*)target, ss, rs, V, tokens, cidx,
                                                          q, temp, seed, step, N, p.nchunks, w,
                                                          n_acc, out, status);
@@ -509,7 +582,7 @@ using namespace df2;
 
 extern "C" size_t dflash2_verify_workspace_bytes(int B, int N, int V, int dtype) {
   if (B < 1 || N < 1 || N > kMaxN || V < kTopK) return 0;
-  Plan p = make_plan(V, dtype, nullptr, 0, 0);
+  Plan p = make_plan(B, N, V, dtype, nullptr, 0, 0);
   return ws_layout(B, N, p.nchunks, nullptr, nullptr);
 }
 
@@ -526,7 +599,7 @@ extern "C" int dflash2_verify(const void* target, int dtype, int64_t seq_stride,
   if (dtype != DFLASH2_BF16 && dtype != DFLASH2_F32) return DFLASH2_EUNSUPPORTED;
   if (!aligned(ws, kWsAlign) || ws_bytes < dflash2_verify_workspace_bytes(B, N, V, dtype))
     return DFLASH2_EWORKSPACE;
-  Plan p = make_plan(V, dtype, target, seq_stride, row_stride);
+  Plan p = make_plan(B, N, V, dtype, target, seq_stride, row_stride);
   Ws w;
   ws_layout(B, N, p.nchunks, &w, (char*)ws);
   if (dtype == DFLASH2_BF16)

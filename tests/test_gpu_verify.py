@@ -220,3 +220,74 @@ def test_verify_lossless_on_gpu(d2):
     e = tot * p_t.astype(np.float64)
     chi2 = float(((counts - e) ** 2 / e).sum())
     assert chi2 < 37.70, chi2
+
+
+def _special_greedy_rows(rng, V, f32):
+    """Six sequences of 8 rows whose maxima are decided by NaN, signed zeros, ties across
+    lanes, waves, vectors and chunks, the ragged last chunk, and infinities."""
+    B, R = 6, 8
+    x = rng.standard_normal((B, R, V)).astype(np.float32)
+    x[1] = -(np.abs(x[1]) + 1.0)
+    x[4] = -np.inf
+    bits = x.copy().view(np.uint32) if f32 else wl.to_bf16_bits(x)
+    if f32:
+        pnan, nnan, pz, nz, pinf = 0x7FC00001, 0xFFC00000, 0x00000000, 0x80000000, 0x7F800000
+        big = int(np.float32(50.0).view(np.uint32))
+    else:
+        pnan, nnan, pz, nz, pinf = 0x7FC1, 0xFFC0, 0x0000, 0x8000, 0x7F80
+        big = int(wl.to_bf16_bits(np.float32(50.0)))
+    for r in range(R):
+        # sequence 0: NaN of either sign, sometimes both, at random depths
+        pos = rng.choice(V, 3, replace=False)
+        if r % 3 != 1:
+            bits[0, r, pos[0]] = pnan
+        if r % 3 != 0:
+            bits[0, r, pos[1]] = nnan
+        # sequence 1: all negative but two zeros of opposite signs, in either order
+        i1, i2 = sorted(rng.choice(V, 2, replace=False))
+        bits[1, r, i1], bits[1, r, i2] = (nz, pz) if r % 2 == 0 else (pz, nz)
+        # sequence 2: one maximum repeated at indices that differ by a lane, a vector, a
+        # wave and a chunk
+        a = int(rng.integers(0, V - 5000))
+        for d in (0, 1, 4, 8, 256, 512, 1024, 2048, 4096)[r % 4:]:
+            bits[2, r, a + d] = big
+        # sequence 3: maximum at the very start, the very end, and chunk edges
+        at = (0, V - 1, 2047, 2048, V - 2, 1023, 1024, V // 2)[r]
+        bits[3, r, at] = big
+        # sequence 4: all -inf, then +inf twice, then one finite value
+        if r == 1:
+            bits[4, r, [77, 70000]] = pinf
+        elif r >= 2:
+            bits[4, r, rng.integers(0, V)] = big
+    return bits.view(np.float32) if f32 else bits
+
+
+@pytest.mark.parametrize("f32", [False, True])
+def test_verify_greedy_special_rows(d2, f32):
+    # the proposals are each row's first element under the top-16 order (from the oracle's
+    # top-16), so every row's decision is visible in n_accept / out_tokens; then each row
+    # in turn gets a wrong proposal, so that its first element is the emitted token
+    rng = np.random.default_rng(71 + f32)
+    V, N = 248320, 7
+    bits = _special_greedy_rows(rng, V, f32)
+    B = bits.shape[0]
+    first = np.stack([orc.topk16_rows(bits[b])[0][:, 0] for b in range(B)]).astype(np.int32)
+    cand = np.stack([np.stack([rng.choice(V, 16, replace=False) for _ in range(N)])
+                     for _ in range(B)]).astype(np.int32)
+    slot = rng.integers(0, 16, (B, N)).astype(np.int32)
+    for b in range(B):
+        for j in range(N):
+            if first[b, j] not in cand[b, j]:
+                cand[b, j, slot[b, j]] = first[b, j]
+            slot[b, j] = int(np.where(cand[b, j] == first[b, j])[0][0])
+    q = rng.dirichlet(np.ones(16), (B, N)).astype(np.float32)
+    temps = np.zeros(B, np.float32)
+    for wrong in [None] + list(range(N)):
+        s = slot.copy()
+        if wrong is not None:
+            s[:, wrong] = (s[:, wrong] + 1) % 16
+        tok = np.take_along_axis(cand, s[..., None], axis=2)[..., 0].astype(np.int32)
+        n, out, st = run_both(d2, bits, not f32, B, N, (N + 1) * V, V, V, tok, cand, q, s, temps,
+                              1, 0, what=f"greedy special rows f32={f32} wrong={wrong}")
+        if wrong is None:
+            assert np.all(n == N)
