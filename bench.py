@@ -8,8 +8,9 @@ seeded synthetic tensors already resident in HBM; several input sets are rotated
 the working set exceeds the 256 MiB last-level cache. Each step is one HIP-graph replay.
 
 Prints one JSON line: throughput, a roofline record for the block-attention call (its
-algorithmic bytes over its average duration, measured with HIP events on its stream) and
-the CPU oracle timed on a bounded sample on one host core.
+algorithmic bytes over its average duration, measured with HIP events on its stream), the
+CPU oracle timed on a bounded sample on one host core, and a separate record for the
+output-head projection fused with the top-16 (not part of the step).
 """
 from __future__ import annotations
 
@@ -120,6 +121,8 @@ def main():
     ap.add_argument("--sets", type=int, default=0,
                     help="input sets to rotate (default: enough to exceed the last-level cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-lmhead", action="store_true",
+                    help="skip the separate output-head projection + top-16 measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 1 GiB device copy (calibrates HBM byte counters)")
@@ -252,6 +255,34 @@ def main():
     traffic = traffic_record(cfg.cfg)
     mean_acc = float(o.n_accept.float().mean().item())
 
+    # The output-head projection fused with the top-16 (a call outside the step): the
+    # drafter's rows 1..N against a synthetic V x C bf16 head, ~N(0, 1/C), generated on the
+    # device from a fixed seed. Its algorithmic bytes are one read of the head and of the
+    # hidden rows.
+    lmhead = None
+    if not args.no_lmhead:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(0xDF2 + cfg.cfg)
+        head = torch.randn((V, cfg.C), generator=gen, device=dev, dtype=torch.float32)
+        head = (head * (1.0 / math.sqrt(cfg.C))).to(torch.bfloat16)
+        hid = torch.from_numpy(wl.head_hidden(cfg).view(np.int16)).view(torch.bfloat16).to(dev)
+        lm_idx = torch.empty((B, N, 16), dtype=torch.int32, device=dev)
+        lm_val = torch.empty((B, N, 16), dtype=torch.float32, device=dev)
+        lm_ws = d2.workspace(d2.lmhead_topk16_workspace_bytes(B, N, V, cfg.C), dev)
+
+        def lm_call(r):
+            d2.lmhead_topk16(hid, B, N, 1, P * cfg.C, cfg.C, head, idx=lm_idx, val=lm_val, ws=lm_ws)
+
+        lm_call(0)
+        torch.cuda.synchronize()
+        lm_ms = timed(lm_call, 4, replays=3)
+        lm_bytes = float(V * cfg.C * 2 + B * N * cfg.C * 2 + B * N * 16 * 8)
+        lm_gbs = lm_bytes / (lm_ms * 1e-3) / 1e9
+        lmhead = {"call": "dflash2_lmhead_topk16", "rows": B * N, "width": cfg.C, "vocab": V,
+                  "us_per_call": lm_ms * 1e3, "bytes_per_call": lm_bytes, "achieved": lm_gbs,
+                  "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": lm_gbs / HBM_PEAK_GBS}
+        del head
+
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -287,6 +318,7 @@ def main():
         "ms_per_step_host_sync": ms_sync,
         "mean_accepted": mean_acc,
         "cpu_baseline": None,
+        "lmhead_topk16": lmhead,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")

@@ -22,6 +22,7 @@
 // the list) is instead reduced exactly, by 16 rounds of a wave maximum of packed words
 // over canonical keys, and its 16 best appended.
 #include "common.hpp"
+#include "merge16.hpp"
 
 namespace df2 {
 namespace {
@@ -29,18 +30,6 @@ namespace {
 constexpr int kThreads = kChunkThreads;
 
 #define DF2_LDS(p) ((__attribute__((address_space(3))) void*)(p))
-
-// the 16th largest of the wave's 64 values (bitwise search on ballots; all lanes call)
-template <int KB>
-__device__ __forceinline__ uint32_t wave_kth16(uint32_t v) {
-  uint32_t prefix = 0;
-#pragma unroll
-  for (int bit = KB - 1; bit >= 0; --bit) {
-    const uint32_t c = prefix | (1u << bit);
-    if (__popcll(__ballot(v >= c)) >= kTopK) prefix = c;
-  }
-  return prefix;
-}
 
 constexpr int kWaves = kThreads / 64;
 #ifndef DF2_TOPK_WCAP
@@ -401,95 +390,23 @@ __global__ __launch_bounds__(kThreads) void topk_wave_scalar_kernel(
   if (lane < kTopK) out[lane] = best;
 }
 
-// Merge the lists of one row (16 packed words each, best first) and write the top-16
-// (index and widened value). A threshold key Tk is found first: each thread takes the
-// largest key among its lists' maxima, and Tk is the largest over the waves of the 16th
-// largest of those (ballot search), so at least 16 list maxima reach it and every top-16
-// entry has a key >= Tk. Only lists whose maximum reaches Tk are read, and their entries
-// with a key >= Tk are ranked directly. If ties make that set too large, the exact 16th
-// largest list maximum T is used instead: at most 16 lists have a maximum >= T.
-constexpr int kMCap = 512;
-
+// The value reported for a merged candidate: the row element itself, widened to binary32.
 template <class KT>
-__global__ __launch_bounds__(kThreads) void topk_merge_kernel(
-    const typename KT::elem_t* __restrict__ scores, int64_t seq_stride, int64_t row_stride,
-    int row0, int N, int nlists, const uint64_t* __restrict__ ws, int32_t* __restrict__ idx,
-    float* __restrict__ val) {
-  extern __shared__ uint64_t cmax[];  // nlists list maxima
-  __shared__ uint64_t cand[kMCap];
-  __shared__ uint32_t wthr[kWaves];
-  __shared__ uint64_t thr;
-  __shared__ int count;
-  const int rowid = blockIdx.x;
-  const int b = rowid / N, r = rowid % N;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const uint64_t* src = ws + (int64_t)rowid * nlists * kTopK;
-  if (t == 0) count = 0;
-  uint32_t kl = 0;
-  for (int c = t; c < nlists; c += kThreads) {
-    const uint64_t v = src[c * kTopK];
-    cmax[c] = v;
-    const uint32_t k = cand_key(v);
-    kl = k > kl ? k : kl;
+struct ElementValue {
+  const typename KT::elem_t* scores;
+  int64_t seq_stride, row_stride;
+  int row0, N;
+  __device__ float operator()(int rowid, uint32_t x, uint32_t /*key*/) const {
+    const int b = rowid / N, r = rowid % N;
+    const typename KT::elem_t* row = scores + (int64_t)b * seq_stride + (int64_t)(row0 + r) * row_stride;
+    uint32_t u;
+    if constexpr (sizeof(typename KT::elem_t) == 2)
+      u = reinterpret_cast<const uint16_t*>(row)[x];
+    else
+      u = __float_as_uint(reinterpret_cast<const float*>(row)[x]);
+    return KT::widen(u);
   }
-  const uint32_t tw = wave_kth16<32>(kl);
-  if (lane == 0) wthr[w] = tw;
-  __syncthreads();
-  uint32_t Tk = wthr[0];
-#pragma unroll
-  for (int i = 1; i < kWaves; ++i) Tk = wthr[i] > Tk ? wthr[i] : Tk;
-  uint64_t T = (uint64_t)Tk << 32;  // the smallest packed word with key Tk
-  for (int pass = 0; pass < 2; ++pass) {
-    for (int c = t; c < nlists; c += kThreads) {
-      if (cmax[c] == 0 || cmax[c] < T) continue;
-      const u32x4_t* l4 = reinterpret_cast<const u32x4_t*>(src + (int64_t)c * kTopK);
-      u32x4_t q[kTopK / 2];
-#pragma unroll
-      for (int i = 0; i < kTopK / 2; ++i) q[i] = l4[i];
-#pragma unroll
-      for (int i = 0; i < kTopK; ++i) {
-        const uint64_t v = ((uint64_t)q[i / 2][2 * (i & 1) + 1] << 32) | q[i / 2][2 * (i & 1)];
-        if (v != 0 && v >= T) {
-          const int pos = atomicAdd(&count, 1);
-          if (pos < kMCap) cand[pos] = v;
-        }
-      }
-    }
-    __syncthreads();
-    if (count <= kMCap || pass == 1) break;
-    // too many ties: the exact 16th largest list maximum
-    if (t == 0) thr = 0;
-    __syncthreads();
-    for (int c = t; c < nlists; c += kThreads) {
-      const uint64_t v = cmax[c];
-      int rank = 0;
-      for (int o = 0; o < nlists; ++o) rank += cmax[o] > v;
-      if (rank == kTopK - 1) thr = v;
-    }
-    __syncthreads();
-    T = thr;
-    if (t == 0) count = 0;
-    __syncthreads();
-  }
-  const int m = count < kMCap ? count : kMCap;
-  const typename KT::elem_t* row =
-      scores + (int64_t)b * seq_stride + (int64_t)(row0 + r) * row_stride;
-  for (int c = t; c < m; c += kThreads) {
-    const uint64_t v = cand[c];
-    int rank = 0;
-    for (int o = 0; o < m; ++o) rank += cand[o] > v;
-    if (rank < kTopK) {
-      const uint32_t x = cand_idx(v);
-      uint32_t u;
-      if constexpr (sizeof(typename KT::elem_t) == 2)
-        u = reinterpret_cast<const uint16_t*>(row)[x];
-      else
-        u = __float_as_uint(reinterpret_cast<const float*>(row)[x]);
-      idx[(int64_t)rowid * kTopK + rank] = (int32_t)x;
-      val[(int64_t)rowid * kTopK + rank] = KT::widen(u);
-    }
-  }
-}
+};
 
 struct Plan {
   int nv;       // 16-byte vectors per lane per wave sub-chunk
@@ -546,7 +463,8 @@ void launch_all(const Plan& p, const void* scores, int64_t ss, int64_t rs, int r
                                                              p.nseg, ws);
   const int nlists = p.nseg * kWaves;
   const size_t lds = (size_t)nlists * sizeof(uint64_t);
-  topk_merge_kernel<KT><<<B * N, kThreads, lds, st>>>(sc, ss, rs, row0, N, nlists, ws, idx, val);
+  merge16_kernel<ElementValue<KT>><<<B * N, kThreads, lds, st>>>(
+      nlists, ws, idx, val, ElementValue<KT>{sc, ss, rs, row0, N});
 }
 
 }  // namespace

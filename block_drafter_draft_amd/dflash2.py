@@ -42,6 +42,8 @@ SIGNATURES = {
     "dflash2_dynconv2": ([_vp] * 4 + [_i32] * 5 + [_vp], _i32),
     "dflash2_topk16": ([_vp, _i32, _i32, _i32, _i32, _i64, _i64, _i32, _vp, _vp, _vp, _sz, _vp], _i32),
     "dflash2_topk16_workspace_bytes": ([_i32] * 4, _sz),
+    "dflash2_lmhead_topk16": ([_vp, _i64, _i64, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp], _i32),
+    "dflash2_lmhead_topk16_workspace_bytes": ([_i32] * 4, _sz),
     "dflash2_select": ([_vp] * 5 + [_i32, _i32, _vp, _vp, _u64, _u64, _i32, _i32] + [_vp] * 5 + [_sz, _vp], _i32),
     "dflash2_select_workspace_bytes": ([_i32] * 2, _sz),
     "dflash2_verify": ([_vp, _i32, _i64, _i64, _i32] + [_vp] * 5 + [_u64, _u64, _i32, _i32] + [_vp] * 4 + [_sz, _vp], _i32),
@@ -179,6 +181,33 @@ def topk16(scores, B, N, row0, seq_stride, row_stride, V, idx=None, val=None, ws
     rc = _lib.dflash2_topk16(_ptr(scores), dt, B, N, row0, seq_stride, row_stride, V, _ptr(idx),
                              _ptr(val), _ptr(ws), ws.numel(), _stream(stream))
     _check(rc, "dflash2_topk16")
+    return idx, val
+
+
+def lmhead_topk16_workspace_bytes(B, N, V, C) -> int:
+    return int(_lib.dflash2_lmhead_topk16_workspace_bytes(B, N, V, C))
+
+
+def lmhead_topk16(hidden, B, N, row0, seq_stride, row_stride, weight, idx=None, val=None,
+                  ws=None, stream=None):
+    """Top-16 of hidden-row x output-head logits; hidden bf16 rows addressed by element
+    strides, weight bf16 [V, C]."""
+    _dev(hidden, weight)
+    _contig(weight)
+    if hidden.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+        raise TypeError("hidden and weight must be bfloat16")
+    V, C = weight.shape
+    dev = hidden.device
+    if idx is None:
+        idx = torch.empty((B, N, K), dtype=torch.int32, device=dev)
+    if val is None:
+        val = torch.empty((B, N, K), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(lmhead_topk16_workspace_bytes(B, N, V, C), dev)
+    rc = _lib.dflash2_lmhead_topk16(_ptr(hidden), seq_stride, row_stride, row0, _ptr(weight), C,
+                                    V, B, N, _ptr(idx), _ptr(val), _ptr(ws), ws.numel(),
+                                    _stream(stream))
+    _check(rc, "dflash2_lmhead_topk16")
     return idx, val
 
 

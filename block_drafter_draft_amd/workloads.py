@@ -123,6 +123,7 @@ CONFIGS = {
 _T_CTX, _T_Q, _T_KBLK, _T_VBLK, _T_KRING, _T_VRING = 1, 2, 3, 4, 5, 6
 _T_X, _T_BASE, _T_DELTA = 7, 8, 9
 _T_DRAFT, _T_TNOISE, _T_PRED, _T_SUCC, _T_GATE, _T_ANCHOR = 10, 11, 12, 13, 14, 15
+_T_HIDDEN, _T_HEAD = 16, 17
 
 
 def _rng(cfg: Config, tensor: int, *more: int) -> np.random.Generator:
@@ -230,6 +231,25 @@ def codebooks(cfg: Config):
 
 def gate(cfg: Config, seqs=None, iset: int = 0) -> np.ndarray:
     return _per_seq(cfg, _T_GATE, 0, seqs, iset, (cfg.N, cfg.R), _normal)
+
+
+def head_hidden(cfg: Config, seqs=None, iset: int = 0) -> np.ndarray:
+    """Final hidden states [B, P, C] bf16 bits ~ N(0, draft_var), the rows the output head
+    projects (rows 1..P-1 are the proposals)."""
+    x = _per_seq(cfg, _T_HIDDEN, 0, seqs, iset, (cfg.P, cfg.C),
+                 lambda r, s: _normal(r, s, cfg.draft_var))
+    return to_bf16_bits(x)
+
+
+def head_weight(cfg: Config, V: int | None = None, chunk: int = 16384) -> np.ndarray:
+    """Output head [V, C] bf16 bits ~ N(0, 1/C), so that logits have variance about
+    draft_var. Generated in row chunks (one stream per chunk) to bound host memory."""
+    V = cfg.V if V is None else V
+    out = np.empty((V, cfg.C), dtype=np.uint16)
+    for c, v0 in enumerate(range(0, V, chunk)):
+        v1 = min(V, v0 + chunk)
+        out[v0:v1] = to_bf16_bits(_normal(_rng(cfg, _T_HEAD, c), (v1 - v0, cfg.C), 1.0 / cfg.C))
+    return out
 
 
 def anchor(cfg: Config, iset: int = 0) -> np.ndarray:

@@ -134,6 +134,30 @@ int dflash2_topk16(const void *scores, int dtype, int B, int N, int row0, int64_
 size_t dflash2_topk16_workspace_bytes(int B, int N, int V, int dtype);
 
 /*
+ * dflash2_lmhead_topk16 - the drafter's output-head projection fused with the top-16
+ * ("Geramy/LSE docs/DFLASH2.md", drafter-geometry paragraph: the drafter shares the
+ * target's output head; "qwen35: DSpark speculative decoding (Qwen3.8-27B drafters) -
+ * #625", DFlash 2 commit: the selector takes the top-k head candidates per block position).
+ *
+ *   logit[b,r,v] = sum_c hidden[b*hid_seq_stride + (row0 + r)*hid_row_stride + c] * weight[v*C + c]
+ *
+ *   hidden  bf16, rows r < N of each of the B sequences, C elements each
+ *   weight  bf16 [V, C] row-major (an output head's usual layout)
+ *   idx     [B, N, 16] int32, val [B, N, 16] f32: the 16 first (v, logit) under the order
+ *           of dflash2_topk16, taken on the binary32 logits
+ * The bf16 products are exact; they are summed in binary32 in an unspecified order, so a
+ * logit may differ from the exact sum by at most about C * 2^-24 * sum_c |h_c w_c| (and
+ * candidates whose logits lie that close may trade places). The logits are never stored.
+ * A NaN logit is reported as a quiet NaN. Requires C % 128 == 0, 16-byte aligned hidden
+ * and weight with strides that are multiples of 8, V >= 16, B*N <= 65535. Hidden rows are
+ * processed 32 per pass over the weight. Workspace: dflash2_lmhead_topk16_workspace_bytes.
+ */
+int dflash2_lmhead_topk16(const void *hidden, int64_t hid_seq_stride, int64_t hid_row_stride,
+                          int row0, const void *weight, int C, int V, int B, int N, int32_t *idx,
+                          float *val, void *ws, size_t ws_bytes, hipStream_t stream);
+size_t dflash2_lmhead_topk16_workspace_bytes(int B, int N, int V, int C);
+
+/*
  * dflash2_select - the candidate selector ("[Spec Decode] DFlash2: local convolution +
  * candidate selector - #52816", PR description, second item).
  *

@@ -6,8 +6,10 @@ single-threaded reference that the GPU library is checked against. Only the test
 product path (``block_drafter_draft_amd``) never does, and shares no code with it.
 
 Each wrapper marshals numpy arrays into the C functions; the arithmetic and the citations
-of the pages live in the C file. Functions that are pinned by tests are listed in
-``tests/test_oracle_pins.py``.
+of the pages live in the C file. The one exception is the output-head projection (the
+``lmhead_*`` functions at the end), written here with numpy: a binary64 matrix product of
+the exact bf16 values, and the top-16 order applied to its rows. Functions that are pinned
+by tests are listed in ``tests/test_oracle_pins.py``.
 """
 from __future__ import annotations
 
@@ -219,3 +221,59 @@ def verify(target, B, N, seq_stride, row_stride, V, tokens, cand_idx, q, slot, t
                     _p(sl), _p(T), ctypes.c_uint64(seed), ctypes.c_uint64(step), B, N,
                     _p(n_acc), _p(out), _p(st))
     return n_acc, out, st
+
+
+# ------------------------------------------------------------------------------------------
+# Output-head projection fused with the top-16 ("Geramy/LSE docs/DFLASH2.md",
+# drafter-geometry paragraph: the drafter shares the target's output head; "qwen35: DSpark
+# speculative decoding (Qwen3.8-27B drafters) - #625", DFlash 2 commit: the selector takes
+# the top-k head candidates of each block position).
+# ------------------------------------------------------------------------------------------
+
+
+def _bf16_to_f64(h: np.ndarray) -> np.ndarray:
+    return (np.asarray(h, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def lmhead_logits(hidden_rows: np.ndarray, weight: np.ndarray, chunk: int = 8192):
+    """logits[m, v] = sum_c h[m, c] w[v, c] for bf16-bit inputs hidden_rows [M, C] and
+    weight [V, C], in binary64, and the sums of |h[m, c] w[v, c]|. Every product of two bf16
+    values is exact in binary64 and the binary64 sum of C of them is within
+    C * 2^-53 * abs_sum of the exact sum, far inside any binary32 result's error."""
+    h = _bf16_to_f64(hidden_rows)
+    ha = np.abs(h)
+    M, V = h.shape[0], weight.shape[0]
+    L = np.empty((M, V), dtype=np.float64)
+    A = np.empty((M, V), dtype=np.float64)
+    for v0 in range(0, V, chunk):
+        w = _bf16_to_f64(weight[v0:v0 + chunk])
+        L[:, v0:v0 + w.shape[0]] = h @ w.T
+        A[:, v0:v0 + w.shape[0]] = ha @ np.abs(w).T
+    return L, A
+
+
+def top16_order_f64(row: np.ndarray) -> np.ndarray:
+    """Indices of the 16 first elements of a binary64 row under the top-16 order: every NaN
+    by ascending index, then values descending (+inf first, -inf last; -0 equal to +0), equal
+    values by ascending index."""
+    x = np.asarray(row, dtype=np.float64)
+    nan = np.isnan(x)
+    idx = np.arange(x.shape[0])
+    key = np.where(nan, 0.0, x) + 0.0               # -0 -> +0
+    # lexsort: last key is primary; sort NaN first, then by -value, then by index
+    order = np.lexsort((idx, -key, ~nan))
+    return order[:K].astype(np.int32)
+
+
+def lmhead_topk16(hidden, B, N, row0, seq_stride, row_stride, weight):
+    """Top-16 of the output-head logits of rows row0..row0+N-1 of each sequence (hidden is
+    a flat bf16-bit buffer addressed by element strides). Returns (idx [B,N,16],
+    logits [B*N, V], abs_sums [B*N, V]); the reported values are logits at idx."""
+    h = np.ascontiguousarray(hidden, dtype=np.uint16).reshape(-1)
+    C = weight.shape[1]
+    rows = np.stack([h[b * seq_stride + (row0 + r) * row_stride:
+                       b * seq_stride + (row0 + r) * row_stride + C]
+                     for b in range(B) for r in range(N)])
+    L, A = lmhead_logits(rows, weight)
+    idx = np.stack([top16_order_f64(L[m]) for m in range(B * N)]).reshape(B, N, K)
+    return idx, L, A

@@ -672,3 +672,78 @@ def test_attention_live_counts_printed_on_the_pages(orc):
         out = orc.block_attn(q, kb, vb, kr, vr, np.array([L], np.int32), W)
         got = P / out[0, 0, 0, 0]
         assert abs(got - live) < 1e-9, (L, W, got, live)
+
+
+# ----------------------------------------------------------------------------------------
+# Output-head projection + top-16
+# ----------------------------------------------------------------------------------------
+
+def test_lmhead_logits_match_fsum_bruteforce(orc):
+    # every logit against a correctly rounded sum (math.fsum) of the exact bf16 products,
+    # computed element by element in plain Python; the absolute sums likewise
+    import math
+    rng = np.random.default_rng(81)
+    M, C, V = 3, 128, 37
+    h = to_bf16_bits(rng.standard_normal((M, C)).astype(np.float32) * 3)
+    w = to_bf16_bits(rng.standard_normal((V, C)).astype(np.float32) / 8)
+    L, A = orc.lmhead_logits(h, w, chunk=16)
+    hf, wf = bf16_bits_to_f32(h).astype(float), bf16_bits_to_f32(w).astype(float)
+    for m in range(M):
+        for v in range(V):
+            prods = [hf[m, c] * wf[v, c] for c in range(C)]
+            exact = math.fsum(prods)
+            assert abs(L[m, v] - exact) <= C * 2.0**-53 * math.fsum(abs(p) for p in prods)
+            assert A[m, v] == pytest.approx(math.fsum(abs(p) for p in prods), rel=1e-14)
+
+
+def test_lmhead_one_hot_head_selects_known_entries(orc):
+    # weight row v = s_v * e_{c(v)}: logit[m, v] = s_v h[m, c(v)] exactly, so the top-16
+    # is fixed by construction: rows planted with large products in a chosen order
+    rng = np.random.default_rng(82)
+    C, V, B, N = 256, 500, 2, 3
+    hid = np.zeros((B, N + 1, C), np.float32)
+    hid[:] = rng.uniform(-1, 1, size=hid.shape).astype(np.float32)
+    col = rng.integers(0, C, size=V)
+    scale = rng.choice([0.5, 0.25, -0.5], size=V).astype(np.float32)
+    w = np.zeros((V, C), np.float32)
+    w[np.arange(V), col] = scale
+    chosen = rng.choice(V, size=16, replace=False)       # planted winners, best first
+    for rank, v in enumerate(chosen):
+        w[v] = 0
+        w[v, 0] = 1.0
+        w[v, 1] = float(64 - rank)                       # needs hid[., ., 1] = 1
+    hid[:, :, 0] = 0.0
+    hid[:, :, 1] = 1.0
+    hb, wb = to_bf16_bits(hid), to_bf16_bits(w)
+    idx, L, _ = orc.lmhead_topk16(hb, B, N, 1, (N + 1) * C, C, wb)
+    for m in range(B * N):
+        np.testing.assert_array_equal(idx.reshape(B * N, 16)[m], chosen)
+        b, r = divmod(m, N)
+        hv = bf16_bits_to_f32(hb[b, 1 + r]).astype(float)
+        exact = bf16_bits_to_f32(wb).astype(float)[np.arange(V), col] * hv[col]
+        exact[chosen] = [64 - k for k in range(16)]
+        np.testing.assert_array_equal(L[m], exact)
+
+
+def test_lmhead_topk_order_bruteforce_with_ties(orc):
+    # small-integer data: the logits are exact integers with many ties; the top-16 must be
+    # the first 16 of a plain Python sort by (-value, index)
+    rng = np.random.default_rng(83)
+    B, N, C, V = 2, 2, 64, 300
+    hid = rng.integers(-2, 3, size=(B, N, C)).astype(np.float32)
+    w = rng.integers(-1, 2, size=(V, C)).astype(np.float32)
+    w[50] = w[7]                                          # duplicated rows tie exactly
+    w[299] = w[7]
+    idx, L, _ = orc.lmhead_topk16(to_bf16_bits(hid), B, N, 0, N * C, C, to_bf16_bits(w))
+    for m in range(B * N):
+        b, r = divmod(m, N)
+        logits = [float(np.dot(hid[b, r].astype(np.int64), w[v].astype(np.int64))) for v in range(V)]
+        want = sorted(range(V), key=lambda v: (-logits[v], v))[:16]
+        np.testing.assert_array_equal(idx.reshape(-1, 16)[m], want)
+        assert L[m].tolist() == logits
+
+
+def test_lmhead_top16_order_specials(orc):
+    x = np.array([1.0, np.nan, 3.0, -0.0, 0.0, 3.0, -np.inf, np.inf, np.nan] + [-5.0] * 10)
+    np.testing.assert_array_equal(orc.top16_order_f64(x),
+                                  [1, 8, 7, 2, 5, 0, 3, 4, 9, 10, 11, 12, 13, 14, 15, 16])
