@@ -22,7 +22,8 @@ constexpr int kMaxR = 512;
 // LDS row stride in elements: 8 extra bf16 keep rows 16-byte aligned and shift the banks
 __host__ __device__ inline int lat_row_stride(int R) { return ((R + 7) / 8) * 8 + 8; }
 
-template <bool VEC>
+// PER: 16-byte gathers per thread (2 * 16 rows * R / 8 / 256 for R <= 64 * PER)
+template <bool VEC, int PER>
 __global__ __launch_bounds__(256) void select_lattice_kernel(
     const int32_t* __restrict__ cidx, const float* __restrict__ cval,
     const float* __restrict__ gate, const uint16_t* __restrict__ pred_cb,
@@ -40,6 +41,8 @@ __global__ __launch_bounds__(256) void select_lattice_kernel(
   __shared__ int32_t prow[kTopK], srow[kTopK];
 
   const int npred = i == 1 ? 1 : kTopK;
+  // the candidate's value, loaded now so that its latency hides behind the gathers
+  const float cv = cval[((int64_t)b * N + (i - 1)) * kTopK + k];
   if (t < kTopK) {
     int32_t p = i == 1 ? anchor[b] : cidx[((int64_t)b * N + (i - 2)) * kTopK + t];
     int32_t c = cidx[((int64_t)b * N + (i - 1)) * kTopK + t];
@@ -49,31 +52,30 @@ __global__ __launch_bounds__(256) void select_lattice_kernel(
   __syncthreads();
   const float* gi = gate + ((int64_t)b * N + (i - 1)) * R;
   if constexpr (VEC) {
-    // R % 8 == 0: 16-byte row pieces; every load of the thread is issued before any store
+    // R % 8 == 0: 16-byte row pieces. Every load of the thread is issued before any is
+    // used, with no conditions: pieces past the end re-read the last one and invalid rows
+    // read row 0, and both are dropped or zeroed afterwards.
     const int vpr = R / 8;
     const int nvec = (npred + kTopK) * vpr;
-    constexpr int kMaxPer = 2 * kTopK * (512 / 8) / 256;  // R <= 512
-    u32x4_t buf[kMaxPer];
+    u32x4_t buf[PER];
+    bool valid[PER];
 #pragma unroll
-    for (int u = 0; u < kMaxPer; ++u) {
-      const int e = t + 256 * u;
-      buf[u] = u32x4_t{0, 0, 0, 0};
-      if (e < nvec) {
-        const int row = e / vpr, c8 = (e % vpr) * 8;
-        const int32_t r = row < npred ? prow[row] : srow[row - npred];
-        const uint16_t* src = row < npred ? pred_cb : succ_cb;
-        if (r >= 0) buf[u] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)r * R + c8);
-      }
+    for (int u = 0; u < PER; ++u) {
+      const int e = min(t + 256 * u, nvec - 1);
+      const int row = e / vpr, c8 = (e % vpr) * 8;
+      const int32_t r = row < npred ? prow[row] : srow[row - npred];
+      const uint16_t* src = row < npred ? pred_cb : succ_cb;
+      valid[u] = r >= 0;
+      buf[u] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)(r >= 0 ? r : 0) * R + c8);
     }
-    float4 gv = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (t < R / 4) gv = reinterpret_cast<const float4*>(gi)[t];
+    const float4 gv = reinterpret_cast<const float4*>(gi)[t < R / 4 ? t : 0];
 #pragma unroll
-    for (int u = 0; u < kMaxPer; ++u) {
+    for (int u = 0; u < PER; ++u) {
       const int e = t + 256 * u;
       if (e < nvec) {
         const int row = e / vpr, c8 = (e % vpr) * 8;
         uint16_t* dst = row < npred ? A + row * RS : Bm + (row - npred) * RS;
-        *reinterpret_cast<u32x4_t*>(dst + c8) = buf[u];
+        *reinterpret_cast<u32x4_t*>(dst + c8) = valid[u] ? buf[u] : u32x4_t{0, 0, 0, 0};
       }
     }
     if (t < R / 4) reinterpret_cast<float4*>(g)[t] = gv;
@@ -132,8 +134,7 @@ __global__ __launch_bounds__(256) void select_lattice_kernel(
       acc = __fadd_rn(acc, pr);
     }
   }
-  const float v = cval[((int64_t)b * N + (i - 1)) * kTopK + k];
-  lattice[(((int64_t)b * N + (i - 1)) * kTopK + kp) * kTopK + k] = __fadd_rn(v, acc);
+  lattice[(((int64_t)b * N + (i - 1)) * kTopK + kp) * kTopK + k] = __fadd_rn(cv, acc);
 }
 
 __global__ __launch_bounds__(64) void select_path_kernel(
@@ -151,13 +152,38 @@ __global__ __launch_bounds__(64) void select_path_kernel(
   __shared__ float qout[kMaxN][kTopK];
   __shared__ int32_t cid[kMaxN * kTopK];
 
+  // Every input load is issued first, so the prologue is one memory round trip: the
+  // anchor, the temperature, the candidates and their values (up to 4 per lane) and the
+  // lattice (up to kMaxN float4 per lane).
+  constexpr int kPerLane = kMaxN * kTopK / 64 + 1;          // candidates per lane
+  constexpr int kLat4 = kMaxN * kTopK * kTopK / 4 / 64;      // lattice float4 per lane
+  const int ncand = N * kTopK, nlat4 = N * kTopK * kTopK / 4;
+  const int32_t anc = anchor[b];
+  const float temp = temperature[b];
+  int32_t cl[kPerLane];
+  float vl[kPerLane];
+  // (indices past the end are clamped, so that the loads carry no conditions; those
+  // values are never used)
+#pragma unroll
+  for (int u = 0; u < kPerLane; ++u) {
+    const int e = min(lane + 64 * u, ncand - 1);
+    cl[u] = cidx[(int64_t)b * ncand + e];
+    vl[u] = cval[(int64_t)b * ncand + e];
+  }
+  const float4* lat4 = reinterpret_cast<const float4*>(lattice + (int64_t)b * N * kTopK * kTopK);
+  float4 lv[kLat4];
+#pragma unroll
+  for (int u = 0; u < kLat4; ++u) lv[u] = lat4[min(lane + 64 * u, nlat4 - 1)];
+
   // index validity (anchor and every candidate); the candidates stay in LDS for the end
-  int bad = 0;
-  if (lane == 0) bad |= !(anchor[b] >= 0 && anchor[b] < V);
-  for (int e = lane; e < N * kTopK; e += 64) {
-    const int32_t c = cidx[(int64_t)b * N * kTopK + e];
-    cid[e] = c;
-    bad |= !(c >= 0 && c < V);
+  int bad = !(anc >= 0 && anc < V);
+#pragma unroll
+  for (int u = 0; u < kPerLane; ++u) {
+    const int e = lane + 64 * u;
+    if (e < ncand) {
+      cid[e] = cl[u];
+      bad |= !(cl[u] >= 0 && cl[u] < V);
+    }
   }
   const bool ok = wave_or(bad) == 0;
   int st = ok ? 0 : DFLASH2_ST_BADTOKEN;
@@ -165,29 +191,30 @@ __global__ __launch_bounds__(64) void select_path_kernel(
   // scores into LDS; every computed score and value must be finite
   int nonfin = 0;
   if (ok) {
-    // 4 scores per lane per step, several steps in flight
-    const float4* lat4 = reinterpret_cast<const float4*>(lattice + (int64_t)b * N * kTopK * kTopK);
     float* Sf = &S[0][0][0];
-#pragma unroll 4
-    for (int e4 = lane; e4 < N * kTopK * kTopK / 4; e4 += 64) {
-      const float4 s4 = lat4[e4];
-      const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const int e = 4 * e4 + h;
-        const int i = e / (kTopK * kTopK) + 1, kp = (e / kTopK) % kTopK;
-        Sf[e] = sv[h];
-        // slot 1 has the anchor as its only predecessor (row 0)
-        if (!(i == 1 && kp > 0)) nonfin |= !(fabsf(sv[h]) <= 3.40282347e38f);
+    for (int u = 0; u < kLat4; ++u) {
+      const int e4 = lane + 64 * u;
+      if (e4 < nlat4) {
+        const float sv[4] = {lv[u].x, lv[u].y, lv[u].z, lv[u].w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const int e = 4 * e4 + h;
+          const int i = e / (kTopK * kTopK) + 1, kp = (e / kTopK) % kTopK;
+          Sf[e] = sv[h];
+          // slot 1 has the anchor as its only predecessor (row 0)
+          if (!(i == 1 && kp > 0)) nonfin |= !(fabsf(sv[h]) <= 3.40282347e38f);
+        }
       }
     }
-    for (int e = lane; e < N * kTopK; e += 64)
-      nonfin |= !(fabsf(cval[(int64_t)b * N * kTopK + e]) <= 3.40282347e38f);
+#pragma unroll
+    for (int u = 0; u < kPerLane; ++u)
+      if (lane + 64 * u < ncand) nonfin |= !(fabsf(vl[u]) <= 3.40282347e38f);
   }
   const bool finite = wave_or(nonfin) == 0;
   if (ok && !finite) st |= DFLASH2_ST_NONFINITE;
   float invT = 0.0f;
-  const int mode = temp_mode(temperature[b], &invT, &st);
+  const int mode = temp_mode(temp, &invT, &st);
 
   int32_t* tk = tokens + (int64_t)b * N;
   int32_t* sl = slot + (int64_t)b * N;
@@ -304,12 +331,15 @@ extern "C" int dflash2_select(const int32_t* cand_idx, const float* cand_val, co
   const size_t lds = (size_t)2 * kTopK * RS * sizeof(uint16_t) + (size_t)RS * sizeof(float) +
                      (size_t)kTopK * RS * sizeof(float);
   const bool vec = R % 8 == 0 && aligned(pred_cb, 16) && aligned(succ_cb, 16) && aligned(gate, 16);
-  if (vec)
-    select_lattice_kernel<true><<<dim3(N, B), 256, lds, stream>>>(cand_idx, cand_val, gate, pred_cb,
-                                                                 succ_cb, V, R, anchor, N, lattice);
+  if (vec && R <= 256)
+    select_lattice_kernel<true, 4><<<dim3(N, B), 256, lds, stream>>>(
+        cand_idx, cand_val, gate, pred_cb, succ_cb, V, R, anchor, N, lattice);
+  else if (vec)
+    select_lattice_kernel<true, 8><<<dim3(N, B), 256, lds, stream>>>(
+        cand_idx, cand_val, gate, pred_cb, succ_cb, V, R, anchor, N, lattice);
   else
-    select_lattice_kernel<false><<<dim3(N, B), 256, lds, stream>>>(cand_idx, cand_val, gate, pred_cb,
-                                                                  succ_cb, V, R, anchor, N, lattice);
+    select_lattice_kernel<false, 1><<<dim3(N, B), 256, lds, stream>>>(
+        cand_idx, cand_val, gate, pred_cb, succ_cb, V, R, anchor, N, lattice);
   select_path_kernel<<<B, 64, 0, stream>>>(cand_idx, cand_val, V, anchor, temperature, seed, step,
                                            N, lattice, tokens, slot, q, status);
   return launch_status();
