@@ -324,6 +324,23 @@ __global__ __launch_bounds__(kThreads) void verify_finish_kernel(
   __shared__ int32_t cand[kTopK];
   __shared__ float candq[kTopK];
 
+  // The greedy chain's chunk maxima are loaded before the temperature is known (for up to
+  // 128 chunks: wave w takes rows w, w + 4, ..., lane l chunks l and l + 64), so that the
+  // two loads are one memory round trip; a sampled sequence ignores them.
+  constexpr int kRowIt = (kMaxN + 1 + kThreads / 64 - 1) / (kThreads / 64);
+  uint64_t pre[kRowIt][2];
+  __shared__ int32_t dtok[kMaxN];
+  const int32_t my_tok = tokens[(int64_t)b * N + (t < N ? t : 0)];  // the proposals, with them
+  const bool few = nchunks <= 128;
+  if (few) {
+#pragma unroll
+    for (int j = 0; j < kRowIt; ++j) {
+      const int r = min(w + (kThreads / 64) * j, N);
+      const uint64_t* src = ws.best + ((int64_t)b * (N + 1) + r) * nchunks;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) pre[j][i] = src[min(lane + 64 * i, nchunks - 1)];
+    }
+  }
   int st = 0;
   float invT = 0.0f;
   int mode = temp_mode(temperature[b], &invT, &st);
@@ -337,13 +354,26 @@ __global__ __launch_bounds__(kThreads) void verify_finish_kernel(
   const typename KT::elem_t* tb = target + (int64_t)b * seq_stride;
 
   if (mode == 0) {
-    for (int r = w; r <= N; r += kThreads / 64) {
-      uint64_t m = 0;
-      const uint64_t* src = ws.best + ((int64_t)b * (N + 1) + r) * nchunks;
-      for (int c = lane; c < nchunks; c += 64) m = src[c] > m ? src[c] : m;
-      m = wave_max_u64(m);
-      if (lane == 0) rowbest[r] = m;
+    if (few) {
+#pragma unroll
+      for (int j = 0; j < kRowIt; ++j) {
+        const int r = w + (kThreads / 64) * j;
+        uint64_t m = pre[j][0];
+        if (lane + 64 < nchunks) m = pre[j][1] > m ? pre[j][1] : m;
+        if (lane >= nchunks) m = 0;
+        m = wave_max_u64(m);
+        if (lane == 0 && r <= N) rowbest[r] = m;
+      }
+    } else {
+      for (int r = w; r <= N; r += kThreads / 64) {
+        uint64_t m = 0;
+        const uint64_t* src = ws.best + ((int64_t)b * (N + 1) + r) * nchunks;
+        for (int c = lane; c < nchunks; c += 64) m = src[c] > m ? src[c] : m;
+        m = wave_max_u64(m);
+        if (lane == 0) rowbest[r] = m;
+      }
     }
+    if (t < N) dtok[t] = my_tok;
     __syncthreads();
     if (t == 0) {
       int n = 0;
@@ -352,14 +382,14 @@ __global__ __launch_bounds__(kThreads) void verify_finish_kernel(
         const uint64_t m = rowbest[j - 1];
         const int32_t y = (int32_t)cand_idx(m);
         if (cand_key(m) == KT::kNaN) st |= DFLASH2_ST_NONFINITE;
-        if (j <= N && d[j - 1] == y) {
+        if (j <= N && dtok[j - 1] == y) {
           ++n;
           continue;
         }
         emitted = y;
         break;
       }
-      for (int j = 0; j <= N; ++j) out[j] = j < n ? d[j] : (j == n ? emitted : -1);
+      for (int j = 0; j <= N; ++j) out[j] = j < n ? dtok[j] : (j == n ? emitted : -1);
       n_accept[b] = n;
       status[b] |= st;
     }
