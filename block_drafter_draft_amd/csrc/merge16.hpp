@@ -96,12 +96,13 @@ __global__ __launch_bounds__(kMergeThreads) void merge16_kernel(int nlists,
   const int m = count < kMCap ? count : kMCap;
   for (int c = t; c < m; c += kMergeThreads) {
     const uint64_t v = cand[c];
+    const uint32_t x = cand_idx(v);
+    const float value = vf(rowid, x, cand_key(v));  // requested before the rank is known
     int rank = 0;
     for (int o = 0; o < m; ++o) rank += cand[o] > v;
     if (rank < kTopK) {
-      const uint32_t x = cand_idx(v);
       idx[(int64_t)rowid * kTopK + rank] = (int32_t)x;
-      val[(int64_t)rowid * kTopK + rank] = vf(rowid, x, cand_key(v));
+      val[(int64_t)rowid * kTopK + rank] = value;
     }
   }
 }
