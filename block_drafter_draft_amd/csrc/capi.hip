@@ -13,6 +13,8 @@ extern "C" const char* dflash2_status_string(int code) {
     case DFLASH2_ST_ZEROMASS: return "status: sampling row without mass";
     case DFLASH2_ST_BADPROB: return "status: probability outside [0, 1], or sampling on a bf16 target";
     case DFLASH2_ST_BADTEMP: return "status: invalid temperature (treated as greedy)";
+    case DFLASH2_ST_RINGLOST: return "status: rewind past the positions the ring holds";
+    case DFLASH2_ST_BADCOUNT: return "status: ring update count out of range (clamped)";
     default: return "unknown code";
   }
 }

@@ -30,6 +30,8 @@ ST_BADTOKEN = 2
 ST_ZEROMASS = 4
 ST_BADPROB = 8
 ST_BADTEMP = 16
+ST_RINGLOST = 32
+ST_BADCOUNT = 64
 
 K = 16
 
@@ -48,6 +50,7 @@ SIGNATURES = {
     "dflash2_select_workspace_bytes": ([_i32] * 2, _sz),
     "dflash2_verify": ([_vp, _i32, _i64, _i64, _i32] + [_vp] * 5 + [_u64, _u64, _i32, _i32] + [_vp] * 4 + [_sz, _vp], _i32),
     "dflash2_verify_workspace_bytes": ([_i32] * 4, _sz),
+    "dflash2_ring_update": ([_vp] * 7 + [_i32] * 7 + [_vp, _vp], _i32),
     "dflash2_status_string": ([_i32], ctypes.c_char_p),
     "dflash2_version": ([], _i32),
 }
@@ -262,3 +265,17 @@ def verify(target, B, N, seq_stride, row_stride, V, tokens, cand_idx, q, slot, t
                              _stream(stream))
     _check(rc, "dflash2_verify")
     return n_accept, out_tokens, status
+
+
+def ring_update(new_k, new_v, n_new, back, ctx_len, k_ring, v_ring, W, status, stream=None):
+    """Rewind (back >= 0) or reset (back < 0), then append n_new rows; ctx_len and the rings
+    are updated in place, status is OR-ed."""
+    _dev(new_k, new_v, n_new, back, ctx_len, k_ring, v_ring, status)
+    _contig(new_k, new_v, n_new, back, ctx_len, k_ring, v_ring, status)
+    B, Pn, Hkv, D = new_k.shape
+    S = k_ring.shape[1]
+    rc = _lib.dflash2_ring_update(_ptr(new_k), _ptr(new_v), _ptr(n_new), _ptr(back),
+                                  _ptr(ctx_len), _ptr(k_ring), _ptr(v_ring), B, Pn, Hkv, D, S, W,
+                                  _dtype(new_k), _ptr(status), _stream(stream))
+    _check(rc, "dflash2_ring_update")
+    return ctx_len, status

@@ -70,6 +70,9 @@ extern "C" {
                                   requested on a bf16 target (the greedy chain was used) */
 #define DFLASH2_ST_BADTEMP 16  /* a temperature that is negative, NaN, infinite or whose
                                   reciprocal overflows (treated as greedy) */
+#define DFLASH2_ST_RINGLOST 32 /* a rewind went back past positions the ring still holds: the
+                                  next window has stale slots until W - 1 new positions are in */
+#define DFLASH2_ST_BADCOUNT 64 /* a ring update count outside [0, Pn] (clamped) */
 
 /* Temperature classes (select and verify): T == 0 selects greedy; T > 0 and finite with a
  * finite binary32 1/T selects sampling; anything else sets ST_BADTEMP and is greedy. */
@@ -156,6 +159,27 @@ int dflash2_lmhead_topk16(const void *hidden, int64_t hid_seq_stride, int64_t hi
                           int row0, const void *weight, int C, int V, int B, int N, int32_t *idx,
                           float *val, void *ws, size_t ws_bytes, hipStream_t stream);
 size_t dflash2_lmhead_topk16_workspace_bytes(int B, int N, int V, int C);
+
+/*
+ * dflash2_ring_update - keeps a drafter context ring in step with the committed sequence
+ * after verification ("Geramy/LSE docs/DFLASH2.md", native-test notes: cache rewind,
+ * replacement and reset). Position p of sequence b lives in ring slot p mod S (the layout
+ * dflash2_block_attn reads). For each b, in this order:
+ *   1. back[b] < 0 resets the sequence (ctx_len[b] = 0); otherwise the sequence is rewound
+ *      by min(back[b], ctx_len[b]) positions. If the rewound window (positions
+ *      max(0, L' - W + 1) .. L' - 1) is not empty and reaches below the oldest position the
+ *      ring held (max(0, L - S)), DFLASH2_ST_RINGLOST is set: those slots hold later positions.
+ *   2. rows j < n_new[b] of new_k/new_v are written to slots (L' + j) mod S, and
+ *      ctx_len[b] = L' + n_new[b]. A count outside [0, Pn] sets DFLASH2_ST_BADCOUNT and is
+ *      clamped.
+ *   new_k, new_v [B, Pn, Hkv, D] (dtype); k_ring, v_ring [B, S, Hkv, D]; ctx_len [B] in/out;
+ *   n_new, back [B]; status [B] OR-ed. Requires Pn <= 16, Pn <= S, S >= W - 1, Hkv*D*size
+ *   a multiple of 16 bytes and 16-byte aligned arrays. Negative ctx_len values count as 0.
+ */
+int dflash2_ring_update(const void *new_k, const void *new_v, const int32_t *n_new,
+                        const int32_t *back, int32_t *ctx_len, void *k_ring, void *v_ring, int B,
+                        int Pn, int Hkv, int D, int S, int W, int dtype, int32_t *status,
+                        hipStream_t stream);
 
 /*
  * dflash2_select - the candidate selector ("[Spec Decode] DFlash2: local convolution +

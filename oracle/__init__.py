@@ -31,6 +31,8 @@ ST_BADTOKEN = 2
 ST_ZEROMASS = 4
 ST_BADPROB = 8
 ST_BADTEMP = 16
+ST_RINGLOST = 32
+ST_BADCOUNT = 64
 
 K = 16
 
@@ -277,3 +279,40 @@ def lmhead_topk16(hidden, B, N, row0, seq_stride, row_stride, weight):
     L, A = lmhead_logits(rows, weight)
     idx = np.stack([top16_order_f64(L[m]) for m in range(B * N)]).reshape(B, N, K)
     return idx, L, A
+
+
+# ------------------------------------------------------------------------------------------
+# Context-ring maintenance after verification ("Geramy/LSE docs/DFLASH2.md", native-test
+# notes: cache rewind, replacement and reset). Position p of a sequence lives in ring slot
+# p mod S.
+# ------------------------------------------------------------------------------------------
+
+
+def ring_update(new_k, new_v, n_new, back, ctx_len, k_ring, v_ring, S, W, status=None):
+    """For each sequence: back < 0 resets it (L' = 0), else it is rewound by min(back, L)
+    (flagging ST_RINGLOST when the rewound window max(0, L'-W+1) .. L'-1 is not empty and
+    reaches below the oldest held position max(0, L-S)); then rows j < n_new go to slots (L'+j) mod S and the
+    length becomes L' + n_new (a count outside [0, Pn] is clamped and flags ST_BADCOUNT).
+    Returns new (ctx_len, k_ring, v_ring, status) arrays."""
+    kr, vr = np.array(k_ring, copy=True), np.array(v_ring, copy=True)
+    L = np.array(ctx_len, dtype=np.int32, copy=True)
+    st = np.zeros(L.shape[0], np.int32) if status is None else np.array(status, np.int32, copy=True)
+    B, Pn = new_k.shape[0], new_k.shape[1]
+    for b in range(B):
+        Lb = max(int(L[b]), 0)
+        if int(back[b]) < 0:
+            Lr = 0
+        else:
+            Lr = Lb - min(int(back[b]), Lb)
+            need_lo = max(0, Lr - W + 1)
+            if need_lo < Lr and need_lo < max(0, Lb - S):
+                st[b] |= ST_RINGLOST
+        n = int(n_new[b])
+        if n < 0 or n > Pn:
+            st[b] |= ST_BADCOUNT
+            n = min(max(n, 0), Pn)
+        for j in range(n):
+            kr[b, (Lr + j) % S] = new_k[b, j]
+            vr[b, (Lr + j) % S] = new_v[b, j]
+        L[b] = Lr + n
+    return L, kr, vr, st

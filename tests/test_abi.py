@@ -39,10 +39,27 @@ def test_library_exports_every_declared_function():
     assert sorted(d2.SIGNATURES) == names
 
 
+def _declared_arg_counts():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    out = {}
+    for m in re.finditer(r"\b(dflash2_[a-z0-9_]+)\s*\(([^)]*)\)\s*;", text):
+        args = m.group(2).strip()
+        out[m.group(1)] = 0 if args in ("", "void") else args.count(",") + 1
+    return out
+
+
+def test_binding_argument_counts_match_header():
+    counts = _declared_arg_counts()
+    for name, (argt, _) in d2.SIGNATURES.items():
+        assert len(argt) == counts[name], (name, len(argt), counts[name])
+
+
 def test_version_and_status_strings():
     assert d2.lib().dflash2_version() >= 100
     for code in (d2.OK, d2.EINVAL, d2.EUNSUPPORTED, d2.EWORKSPACE, d2.EHIP, d2.ST_NONFINITE,
-                 d2.ST_BADTOKEN, d2.ST_ZEROMASS, d2.ST_BADPROB, d2.ST_BADTEMP):
+                 d2.ST_BADTOKEN, d2.ST_ZEROMASS, d2.ST_BADPROB, d2.ST_BADTEMP, d2.ST_RINGLOST,
+                 d2.ST_BADCOUNT):
         s = d2.status_string(code)
         assert s and s != "unknown code"
     assert d2.status_string(12345) == "unknown code"
@@ -54,7 +71,9 @@ def test_constants_match_header():
                       ("DFLASH2_ST_NONFINITE", d2.ST_NONFINITE),
                       ("DFLASH2_ST_BADTOKEN", d2.ST_BADTOKEN),
                       ("DFLASH2_ST_ZEROMASS", d2.ST_ZEROMASS),
-                      ("DFLASH2_ST_BADPROB", d2.ST_BADPROB), ("DFLASH2_ST_BADTEMP", d2.ST_BADTEMP)]:
+                      ("DFLASH2_ST_BADPROB", d2.ST_BADPROB), ("DFLASH2_ST_BADTEMP", d2.ST_BADTEMP),
+                      ("DFLASH2_ST_RINGLOST", d2.ST_RINGLOST),
+                      ("DFLASH2_ST_BADCOUNT", d2.ST_BADCOUNT)]:
         m = re.search(rf"#define {name} \(?(-?\d+)\)?", text)
         assert m and int(m.group(1)) == val, name
     for name, val in [("DFLASH2_OK", d2.OK), ("DFLASH2_EINVAL", d2.EINVAL),
@@ -186,3 +205,38 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
         d2.dynconv2(torch.zeros(1, 8, 16), torch.zeros(2, 16), torch.zeros(1, 8, 2, 1))
+
+
+def test_lmhead_topk16_rejects():
+    L = d2.lib()
+
+    def call(hid=FAKE, w=FAKE, C=5120, V=248320, B=1, N=7, row0=1, ss=8 * 5120, rs=5120,
+             idx=FAKE, val=FAKE, ws=FAKE, wsb=1 << 30):
+        return L.dflash2_lmhead_topk16(hid, ss, rs, row0, w, C, V, B, N, idx, val, ws, wsb, None)
+    assert call(hid=NUL) == d2.EINVAL
+    assert call(val=NUL) == d2.EINVAL
+    assert call(B=0) == d2.EINVAL
+    assert call(V=15) == d2.EINVAL
+    assert call(row0=-1) == d2.EINVAL
+    assert call(C=5000) == d2.EUNSUPPORTED            # not a multiple of 128
+    assert call(rs=5121) == d2.EUNSUPPORTED           # row stride not a multiple of 8
+    assert call(hid=ctypes.c_void_p(0x100008)) == d2.EUNSUPPORTED
+    assert call(wsb=16) == d2.EWORKSPACE
+    assert d2.lmhead_topk16_workspace_bytes(1, 7, 248320, 5120) > 0
+
+
+def test_ring_update_rejects():
+    L = d2.lib()
+
+    def call(nk=FAKE, B=2, Pn=8, Hkv=8, D=128, S=2048, W=2048, dt=d2.BF16, status=FAKE, kr=FAKE):
+        return L.dflash2_ring_update(nk, FAKE, FAKE, FAKE, FAKE, kr, FAKE, B, Pn, Hkv, D, S, W, dt,
+                                     status, None)
+    assert call(nk=NUL) == d2.EINVAL
+    assert call(status=NUL) == d2.EINVAL
+    assert call(B=0) == d2.EINVAL
+    assert call(S=100, W=2048) == d2.EINVAL            # the ring cannot hold the window
+    assert call(Pn=17) == d2.EUNSUPPORTED
+    assert call(S=4, W=4, Pn=8) == d2.EUNSUPPORTED     # more new rows than slots
+    assert call(dt=9) == d2.EUNSUPPORTED
+    assert call(Hkv=1, D=3) == d2.EUNSUPPORTED         # rows not whole 16-byte pieces
+    assert call(kr=ctypes.c_void_p(0x100008)) == d2.EUNSUPPORTED

@@ -72,7 +72,8 @@ def test_attn_varied_contexts(d2):
 
 @pytest.mark.parametrize("P,Hq,Hkv,D,S,W", [(8, 32, 8, 64, 300, 200), (16, 2, 1, 128, 64, 33),
                                            (8, 8, 8, 128, 40, 40), (3, 5, 1, 64, 100, 1),
-                                           (2, 16, 2, 128, 17, 18), (8, 24, 8, 128, 2048, 2048)])
+                                           (2, 16, 2, 128, 17, 18), (8, 24, 8, 128, 2048, 2048),
+                                           (8, 32, 8, 128, 511, 512), (4, 32, 8, 128, 1000, 1000)])
 def test_attn_shapes(d2, P, Hq, Hkv, D, S, W):
     rng = np.random.default_rng(P * 131 + Hq * 7 + D + S + W)
     L = [0, 1, W - 2 if W > 2 else 0, W + 5, 3 * S + 7]

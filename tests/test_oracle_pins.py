@@ -747,3 +747,79 @@ def test_lmhead_top16_order_specials(orc):
     x = np.array([1.0, np.nan, 3.0, -0.0, 0.0, 3.0, -np.inf, np.inf, np.nan] + [-5.0] * 10)
     np.testing.assert_array_equal(orc.top16_order_f64(x),
                                   [1, 8, 7, 2, 5, 0, 3, 4, 9, 10, 11, 12, 13, 14, 15, 16])
+
+
+# ----------------------------------------------------------------------------------------
+# Context-ring maintenance
+# ----------------------------------------------------------------------------------------
+
+def test_ring_update_against_an_ownership_model(orc):
+    # An independent model keeps the committed sequence (content by position) and, per slot,
+    # which position last wrote it. After every operation the ring must hold each position
+    # of the next window that still owns its slot, and ST_RINGLOST must be set exactly when
+    # a window position had lost its slot at the rewind.
+    rng = np.random.default_rng(84)
+    S, W, Pn = 12, 10, 4
+    L = np.zeros(1, np.int32)
+    kr = np.full((1, S, 1, 2), -1.0, np.float32)
+    vr = kr.copy()
+    hist = []                 # content id by position
+    owner = [-1] * S          # position that last wrote each slot
+    gen = 0
+    for step in range(400):
+        back = int(rng.choice([-1, 0, 0, 0, 1, 2, 3, 5, 40]))
+        n = int(rng.integers(0, Pn + 1))
+        gen += 1
+        content = np.array([[[[gen * 100.0 + j, -gen * 100.0 - j]] for j in range(Pn)]], np.float32)
+        # model
+        Lb = len(hist)
+        if back < 0:
+            Lr, lost = 0, False
+            owner = [-1] * S
+        else:
+            Lr = Lb - min(back, Lb)
+            need = range(max(0, Lr - W + 1), Lr)
+            lost = any(owner[p % S] != p for p in need)
+        hist = hist[:Lr]
+        for j in range(n):
+            hist.append(gen * 100.0 + j)
+            owner[(Lr + j) % S] = Lr + j
+        # oracle
+        L, kr, vr, st = orc.ring_update(content, -content, np.array([n], np.int32),
+                                        np.array([back], np.int32), L, kr, vr, S, W)
+        assert int(L[0]) == len(hist)
+        assert bool(st[0] & orc.ST_RINGLOST) == lost, (step, back, Lb)
+        for p in range(max(0, len(hist) - S), len(hist)):
+            if owner[p % S] == p:
+                assert kr[0, p % S, 0, 0] == hist[p] and vr[0, p % S, 0, 0] == -hist[p]
+
+
+def test_ring_update_plain_appends_fill_slots_by_position(orc):
+    # appends only: slot p mod S holds position p for the last S positions (closed form)
+    S, W, Pn = 7, 5, 3
+    L = np.array([0, 5], np.int32)
+    kr = np.zeros((2, S, 1, 1), np.float32)
+    vr = kr.copy()
+    total = [0, 5]
+    for step in range(20):
+        n = np.array([step % (Pn + 1), (step * 2) % (Pn + 1)], np.int32)
+        new = np.stack([np.arange(total[b], total[b] + Pn, dtype=np.float32).reshape(Pn, 1, 1)
+                        for b in range(2)])
+        L, kr, vr, st = orc.ring_update(new, new, n, np.zeros(2, np.int32), L, kr, vr, S, W)
+        assert not st.any()
+        for b in range(2):
+            total[b] += int(n[b])
+            assert int(L[b]) == total[b]
+            for p in range(max(total[b] - S, 5 if b else 0), total[b]):
+                assert kr[b, p % S, 0, 0] == p
+
+
+def test_ring_update_counts_and_reset(orc):
+    S, W, Pn = 8, 8, 4
+    new = np.ones((3, Pn, 1, 1), np.float32)
+    L, kr, vr, st = orc.ring_update(new, new, np.array([-1, 9, 2], np.int32),
+                                    np.array([0, 0, -1], np.int32), np.array([5, 5, 100], np.int32),
+                                    np.zeros((3, S, 1, 1), np.float32),
+                                    np.zeros((3, S, 1, 1), np.float32), S, W)
+    np.testing.assert_array_equal(L, [5, 9, 2])
+    np.testing.assert_array_equal(st, [orc.ST_BADCOUNT, orc.ST_BADCOUNT, 0])
