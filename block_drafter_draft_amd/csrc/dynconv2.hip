@@ -7,8 +7,8 @@
 //
 // with x[b,-1,c] = 0. One thread owns 8 consecutive channels of one (sequence, position):
 // it loads x at that position and the one before (16-byte loads for bf16), the two base
-// rows and the two coefficients of its group, all independent of each other, so a call is
-// one memory round trip. The neighbour row is re-read from L2, not HBM. The op moves
+// rows and the two coefficients of its group, all independent of each other and issued
+// together, so a call is one memory round trip. The neighbour row is re-read from L2, not HBM. The op moves
 // B*P*C*(2+2) bytes plus the base and coefficients and is bound by memory (or by launch
 // latency at small B).
 #include "common.hpp"
@@ -32,36 +32,39 @@ __device__ __forceinline__ void load8(const void* x, int64_t off, float (&v)[kCP
   }
 }
 
+// Grid: (channel blocks of 128 threads x 8 channels, sequence-position rows). Every load of
+// a thread is issued before any is used: the neighbour row is always read (row 0 reads its
+// own row) and replaced by zeros afterwards, so there is no branch between the loads.
+constexpr int kConvThreads = 128;
+
 template <bool BF16>
-__global__ __launch_bounds__(256) void dynconv2_kernel(const void* __restrict__ x,
-                                                       const float* __restrict__ base,
-                                                       const float* __restrict__ delta,
-                                                       void* __restrict__ out, int B, int P, int C,
-                                                       int G) {
-  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int per_row = C / kCPT;
-  if (tid >= (int64_t)B * P * per_row) return;
-  const int64_t row = tid / per_row;  // b * P + i
-  const int i = (int)(row % P);
-  const int c0 = (int)(tid % per_row) * kCPT;
+__global__ __launch_bounds__(kConvThreads) void dynconv2_kernel(const void* __restrict__ x,
+                                                                const float* __restrict__ base,
+                                                                const float* __restrict__ delta,
+                                                                void* __restrict__ out, int P,
+                                                                int C, int G) {
+  const int row = blockIdx.y;  // b * P + i
+  const int i = row % P;
+  const int c0 = (blockIdx.x * kConvThreads + threadIdx.x) * kCPT;
+  if (c0 >= C) return;
   const int grp = c0 / 16;
+  const int64_t prow = i > 0 ? row - 1 : row;
   float cur[kCPT], prev[kCPT], b0[kCPT], b1[kCPT];
-  load8<BF16>(x, row * C + c0, cur);
-  if (i > 0) {
-    load8<BF16>(x, (row - 1) * C + c0, prev);
-  } else {
-#pragma unroll
-    for (int e = 0; e < kCPT; ++e) prev[e] = 0.0f;
-  }
+  load8<BF16>(x, (int64_t)row * C + c0, cur);
+  load8<BF16>(x, prow * C + c0, prev);
   const float4* bp0 = reinterpret_cast<const float4*>(base + c0);
   const float4* bp1 = reinterpret_cast<const float4*>(base + C + c0);
   const float4 a0 = bp0[0], a1 = bp0[1], e0 = bp1[0], e1 = bp1[1];
+  const float d0 = delta[((int64_t)row * 2 + 0) * G + grp];
+  const float d1 = delta[((int64_t)row * 2 + 1) * G + grp];
   b0[0] = a0.x; b0[1] = a0.y; b0[2] = a0.z; b0[3] = a0.w;
   b0[4] = a1.x; b0[5] = a1.y; b0[6] = a1.z; b0[7] = a1.w;
   b1[0] = e0.x; b1[1] = e0.y; b1[2] = e0.z; b1[3] = e0.w;
   b1[4] = e1.x; b1[5] = e1.y; b1[6] = e1.z; b1[7] = e1.w;
-  const float d0 = delta[(row * 2 + 0) * G + grp];
-  const float d1 = delta[(row * 2 + 1) * G + grp];
+  if (i == 0) {
+#pragma unroll
+    for (int e = 0; e < kCPT; ++e) prev[e] = 0.0f;
+  }
   float y[kCPT];
 #pragma unroll
   for (int e = 0; e < kCPT; ++e) {
@@ -74,9 +77,9 @@ __global__ __launch_bounds__(256) void dynconv2_kernel(const void* __restrict__ 
 #pragma unroll
     for (int h = 0; h < 4; ++h)
       o[h] = (uint32_t)f32_to_bf16(y[2 * h]) | ((uint32_t)f32_to_bf16(y[2 * h + 1]) << 16);
-    *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(out) + row * C + c0) = o;
+    *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(out) + (int64_t)row * C + c0) = o;
   } else {
-    float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + row * C + c0);
+    float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + (int64_t)row * C + c0);
     p[0] = make_float4(y[0], y[1], y[2], y[3]);
     p[1] = make_float4(y[4], y[5], y[6], y[7]);
   }
@@ -96,11 +99,11 @@ extern "C" int dflash2_dynconv2(const void* x, const float* base, const float* d
   if (!aligned(x, 16) || !aligned(out, 16)) return DFLASH2_EUNSUPPORTED;
   if (x == out) return DFLASH2_EINVAL;
   if (!aligned(base, 16)) return DFLASH2_EUNSUPPORTED;
-  const int64_t threads = (int64_t)B * P * (C / kCPT);
-  const int blocks = (int)((threads + 255) / 256);
+  if ((int64_t)B * P > 65535) return DFLASH2_EUNSUPPORTED;
+  const dim3 grid((C / kCPT + kConvThreads - 1) / kConvThreads, B * P);
   if (dtype == DFLASH2_BF16)
-    dynconv2_kernel<true><<<blocks, 256, 0, stream>>>(x, base, delta, out, B, P, C, C / 16);
+    dynconv2_kernel<true><<<grid, kConvThreads, 0, stream>>>(x, base, delta, out, P, C, C / 16);
   else
-    dynconv2_kernel<false><<<blocks, 256, 0, stream>>>(x, base, delta, out, B, P, C, C / 16);
+    dynconv2_kernel<false><<<grid, kConvThreads, 0, stream>>>(x, base, delta, out, P, C, C / 16);
   return launch_status();
 }

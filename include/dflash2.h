@@ -116,7 +116,8 @@ size_t dflash2_block_attn_workspace_bytes(int B, int P, int Hq, int Hkv, int D, 
  *
  *   x, out [B, P, C] (dtype), base [2, C] f32, delta [B, P, 2, C/group] f32.
  * Arithmetic in binary32, each product and sum rounded once, result rounded to dtype.
- * Requires group == 16 and C % 16 == 0, P in [1, 16]. No workspace. out may not alias x.
+ * Requires group == 16 and C % 16 == 0, P in [1, 16], B*P <= 65535. No workspace. out may
+ * not alias x.
  */
 int dflash2_dynconv2(const void *x, const float *base, const float *delta, void *out, int B, int P,
                      int C, int group, int dtype, hipStream_t stream);
