@@ -9,8 +9,9 @@ the working set exceeds the 256 MiB last-level cache. Each step is one HIP-graph
 
 Prints one JSON line: throughput, a roofline record for the block-attention call (its
 algorithmic bytes over its average duration, measured with HIP events on its stream), the
-CPU oracle timed on a bounded sample on one host core, and a separate record for the
-output-head projection fused with the top-16 (not part of the step).
+CPU oracle timed on a bounded sample on one host core, and separate records for the
+output-head projection fused with the top-16 and for the selector over Q8 codebooks
+(neither is part of the step).
 """
 from __future__ import annotations
 
@@ -123,6 +124,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-lmhead", action="store_true",
                     help="skip the separate output-head projection + top-16 measurement")
+    ap.add_argument("--no-q8", action="store_true",
+                    help="skip the separate selector-over-Q8-codebooks measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 1 GiB device copy (calibrates HBM byte counters)")
@@ -283,6 +286,32 @@ def main():
                   "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": lm_gbs / HBM_PEAK_GBS}
         del head
 
+    # The selector over affine-Q8 codebooks (a call outside the step): the workload's bf16
+    # codebooks converted to Q8 (groups of 64), same candidates, gates and anchors.
+    select_q8 = None
+    if not args.no_q8 and cfg.R % 64 == 0:
+        pq, sq = wl.q8_quantize(wl.bf16_bits_to_f32(cb[0])), wl.q8_quantize(wl.bf16_bits_to_f32(cb[1]))
+
+        def q8_dev(t):
+            codes = torch.from_numpy(np.ascontiguousarray(t[0])).to(dev)
+            sc = torch.from_numpy(t[1].view(np.int16)).view(torch.bfloat16).to(dev)
+            bi = torch.from_numpy(t[2].view(np.int16)).view(torch.bfloat16).to(dev)
+            return codes, sc, bi
+        pq_d, sq_d = q8_dev(pq), q8_dev(sq)
+        del pq, sq
+
+        def q8_call(r):
+            x = inputs[r % nsets]
+            d2.select_q8(o.cand_idx, o.cand_val, x.gate, pq_d, sq_d, x.anchor, x.temperature,
+                         cfg.seed, r, tokens=o.tokens, slot=o.slot, q=o.q, status=o.status,
+                         ws=runner.ws_sel)
+
+        q8_call(0)
+        torch.cuda.synchronize()
+        select_q8 = {"call": "dflash2_select_q8", "us_per_call": timed(q8_call, reps) * 1e3,
+                     "bf16_select_us_per_call": stage_ms["select"] * 1e3}
+        del pq_d, sq_d
+
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -319,6 +348,7 @@ def main():
         "mean_accepted": mean_acc,
         "cpu_baseline": None,
         "lmhead_topk16": lmhead,
+        "select_q8": select_q8,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")

@@ -137,6 +137,102 @@ __global__ __launch_bounds__(256) void select_lattice_kernel(
   lattice[(((int64_t)b * N + (i - 1)) * kTopK + kp) * kTopK + k] = __fadd_rn(cv, acc);
 }
 
+// Affine-Q8 codebooks ("Geramy/LSE docs/DFLASH2.md", conversion notes: selector codebooks
+// in affine Q8 with groups of 64, BF16 scale and bias, FP32 activations and accumulation):
+// element r of a row is fl(fl(scale * q) + bias), q its unsigned 8-bit code and scale, bias
+// those of its group of 64, widened from bf16. Same lattice as above: each thread gathers
+// 16-byte code pieces with their group's scale and bias (and, for predecessor rows, the
+// gate), every load issued before any is used; predecessor rows are dequantised straight
+// into fl(A g) and successor rows into binary32, both in LDS; then thread (kp, k) sums
+// fl(fl(A g) B) left to right over r. PER: code pieces per thread (R / 16 * 32 / 256).
+template <int PER>
+__global__ __launch_bounds__(256) void select_lattice_q8_kernel(
+    const int32_t* __restrict__ cidx, const float* __restrict__ cval,
+    const float* __restrict__ gate, const uint8_t* __restrict__ pcodes,
+    const uint16_t* __restrict__ pscale, const uint16_t* __restrict__ pbias,
+    const uint8_t* __restrict__ scodes, const uint16_t* __restrict__ sscale,
+    const uint16_t* __restrict__ sbias, int V, int R, const int32_t* __restrict__ anchor, int N,
+    float* __restrict__ lattice) {
+  extern __shared__ uint8_t smem[];
+  const int i = blockIdx.x + 1;  // slot 1..N
+  const int b = blockIdx.y;
+  const int t = threadIdx.x;
+  const int kp = t >> 4, k = t & 15;
+  const int RS = R + 4;                               // floats per LDS row (16-byte aligned)
+  float* AG = reinterpret_cast<float*>(smem);         // [16][RS] fl(A g)
+  float* Bf = AG + 16 * RS;                           // [16][RS] successor rows
+  __shared__ int32_t prow[kTopK], srow[kTopK];
+
+  const int npred = i == 1 ? 1 : kTopK;
+  const float cv = cval[((int64_t)b * N + (i - 1)) * kTopK + k];
+  if (t < kTopK) {
+    int32_t p = i == 1 ? anchor[b] : cidx[((int64_t)b * N + (i - 2)) * kTopK + t];
+    int32_t c = cidx[((int64_t)b * N + (i - 1)) * kTopK + t];
+    prow[t] = (p >= 0 && p < V) ? p : -1;  // invalid indices are never gathered
+    srow[t] = (c >= 0 && c < V) ? c : -1;
+  }
+  __syncthreads();
+  const float* gi = gate + ((int64_t)b * N + (i - 1)) * R;
+  const int ppr = R / 16, G = R / 64;
+  const int npieces = (npred + kTopK) * ppr;
+  u32x4_t code[PER];
+  float sc[PER], bi[PER];
+  float4 gq[PER][4];
+  bool valid[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int e = min(t + 256 * u, npieces - 1);
+    const int row = e / ppr, c16 = (e % ppr) * 16;
+    const bool isp = row < npred;
+    const int32_t r = isp ? prow[row] : srow[row - npred];
+    valid[u] = r >= 0;
+    const int64_t rr = r >= 0 ? r : 0;
+    code[u] = *reinterpret_cast<const u32x4_t*>((isp ? pcodes : scodes) + rr * R + c16);
+    sc[u] = bf16_to_f32((isp ? pscale : sscale)[rr * G + c16 / 64]);
+    bi[u] = bf16_to_f32((isp ? pbias : sbias)[rr * G + c16 / 64]);
+    const float4* g4 = reinterpret_cast<const float4*>(gi + c16);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) gq[u][h] = g4[h];
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int e = t + 256 * u;
+    if (e < npieces) {
+      const int row = e / ppr, c16 = (e % ppr) * 16;
+      const bool isp = row < npred;
+      float* dst = isp ? AG + row * RS + c16 : Bf + (row - npred) * RS + c16;
+      const float gv[16] = {gq[u][0].x, gq[u][0].y, gq[u][0].z, gq[u][0].w,
+                            gq[u][1].x, gq[u][1].y, gq[u][1].z, gq[u][1].w,
+                            gq[u][2].x, gq[u][2].y, gq[u][2].z, gq[u][2].w,
+                            gq[u][3].x, gq[u][3].y, gq[u][3].z, gq[u][3].w};
+      float v[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const float code_q = (float)((code[u][q / 4] >> (8 * (q & 3))) & 0xffu);
+        float a = valid[u] ? __fadd_rn(__fmul_rn(sc[u], code_q), bi[u]) : 0.0f;
+        v[q] = isp ? __fmul_rn(a, gv[q]) : a;
+      }
+#pragma unroll
+      for (int q = 0; q < 16; q += 4)
+        *reinterpret_cast<float4*>(dst + q) = make_float4(v[q], v[q + 1], v[q + 2], v[q + 3]);
+    }
+  }
+  __syncthreads();
+  if (kp >= npred) return;
+  const float* ag = AG + kp * RS;
+  const float* bb = Bf + k * RS;
+  float acc = 0.0f;
+  for (int r = 0; r < R; r += 4) {
+    const float4 a4 = *reinterpret_cast<const float4*>(ag + r);
+    const float4 b4 = *reinterpret_cast<const float4*>(bb + r);
+    acc = __fadd_rn(acc, __fmul_rn(a4.x, b4.x));
+    acc = __fadd_rn(acc, __fmul_rn(a4.y, b4.y));
+    acc = __fadd_rn(acc, __fmul_rn(a4.z, b4.z));
+    acc = __fadd_rn(acc, __fmul_rn(a4.w, b4.w));
+  }
+  lattice[(((int64_t)b * N + (i - 1)) * kTopK + kp) * kTopK + k] = __fadd_rn(cv, acc);
+}
+
 __global__ __launch_bounds__(64) void select_path_kernel(
     const int32_t* __restrict__ cidx, const float* __restrict__ cval, int V,
     const int32_t* __restrict__ anchor, const float* __restrict__ temperature, uint64_t seed,
@@ -340,6 +436,41 @@ extern "C" int dflash2_select(const int32_t* cand_idx, const float* cand_val, co
   else
     select_lattice_kernel<false, 1><<<dim3(N, B), 256, lds, stream>>>(
         cand_idx, cand_val, gate, pred_cb, succ_cb, V, R, anchor, N, lattice);
+  select_path_kernel<<<B, 64, 0, stream>>>(cand_idx, cand_val, V, anchor, temperature, seed, step,
+                                           N, lattice, tokens, slot, q, status);
+  return launch_status();
+}
+
+extern "C" int dflash2_select_q8(const int32_t* cand_idx, const float* cand_val,
+                                 const float* gate, const uint8_t* pred_codes,
+                                 const uint16_t* pred_scale, const uint16_t* pred_bias,
+                                 const uint8_t* succ_codes, const uint16_t* succ_scale,
+                                 const uint16_t* succ_bias, int V, int R, const int32_t* anchor,
+                                 const float* temperature, uint64_t seed, uint64_t step, int B,
+                                 int N, int32_t* tokens, int32_t* slot, float* q, int32_t* status,
+                                 void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!cand_idx || !cand_val || !gate || !pred_codes || !pred_scale || !pred_bias ||
+      !succ_codes || !succ_scale || !succ_bias || !anchor || !temperature || !tokens || !slot ||
+      !q || !status || !ws)
+    return DFLASH2_EINVAL;
+  if (B < 1 || N < 1 || R < 1 || V < kTopK) return DFLASH2_EINVAL;
+  if (N > kMaxN || R > kMaxR || R % 64 != 0 || B > 65535) return DFLASH2_EUNSUPPORTED;
+  if (!aligned(pred_codes, 16) || !aligned(succ_codes, 16) || !aligned(gate, 16) ||
+      !aligned(pred_scale, 2) || !aligned(pred_bias, 2) || !aligned(succ_scale, 2) ||
+      !aligned(succ_bias, 2))
+    return DFLASH2_EUNSUPPORTED;
+  if (!aligned(ws, kWsAlign) || ws_bytes < dflash2_select_workspace_bytes(B, N))
+    return DFLASH2_EWORKSPACE;
+  float* lattice = (float*)ws;
+  const size_t lds = (size_t)2 * kTopK * (R + 4) * sizeof(float);
+  if (R <= 256)
+    select_lattice_q8_kernel<2><<<dim3(N, B), 256, lds, stream>>>(
+        cand_idx, cand_val, gate, pred_codes, pred_scale, pred_bias, succ_codes, succ_scale,
+        succ_bias, V, R, anchor, N, lattice);
+  else
+    select_lattice_q8_kernel<4><<<dim3(N, B), 256, lds, stream>>>(
+        cand_idx, cand_val, gate, pred_codes, pred_scale, pred_bias, succ_codes, succ_scale,
+        succ_bias, V, R, anchor, N, lattice);
   select_path_kernel<<<B, 64, 0, stream>>>(cand_idx, cand_val, V, anchor, temperature, seed, step,
                                            N, lattice, tokens, slot, q, status);
   return launch_status();

@@ -48,6 +48,7 @@ SIGNATURES = {
     "dflash2_lmhead_topk16_workspace_bytes": ([_i32] * 4, _sz),
     "dflash2_select": ([_vp] * 5 + [_i32, _i32, _vp, _vp, _u64, _u64, _i32, _i32] + [_vp] * 5 + [_sz, _vp], _i32),
     "dflash2_select_workspace_bytes": ([_i32] * 2, _sz),
+    "dflash2_select_q8": ([_vp] * 9 + [_i32, _i32, _vp, _vp, _u64, _u64, _i32, _i32] + [_vp] * 5 + [_sz, _vp], _i32),
     "dflash2_verify": ([_vp, _i32, _i64, _i64, _i32] + [_vp] * 5 + [_u64, _u64, _i32, _i32] + [_vp] * 4 + [_sz, _vp], _i32),
     "dflash2_verify_workspace_bytes": ([_i32] * 4, _sz),
     "dflash2_ring_update": ([_vp] * 7 + [_i32] * 7 + [_vp, _vp], _i32),
@@ -239,6 +240,32 @@ def select(cand_idx, cand_val, gate, pred_cb, succ_cb, anchor, temperature, seed
                              _ptr(tokens), _ptr(slot), _ptr(q), _ptr(status), _ptr(ws),
                              ws.numel(), _stream(stream))
     _check(rc, "dflash2_select")
+    return tokens, slot, q, status
+
+
+def select_q8(cand_idx, cand_val, gate, pred_q8, succ_q8, anchor, temperature, seed, step,
+              tokens=None, slot=None, q=None, status=None, ws=None, stream=None):
+    """pred_q8 / succ_q8: (codes uint8 [V, R], scale bf16 [V, R/64], bias bf16 [V, R/64])."""
+    _dev(cand_idx, cand_val, gate, anchor, temperature, *pred_q8, *succ_q8)
+    _contig(cand_idx, cand_val, gate, anchor, temperature, *pred_q8, *succ_q8)
+    B, N, _ = cand_idx.shape
+    V, R = pred_q8[0].shape
+    for cb in (pred_q8, succ_q8):
+        if cb[0].dtype != torch.uint8 or cb[1].dtype != torch.bfloat16 or cb[2].dtype != torch.bfloat16:
+            raise TypeError("Q8 codebooks: uint8 codes, bfloat16 scale and bias")
+    dev = cand_idx.device
+    tokens = torch.empty((B, N), dtype=torch.int32, device=dev) if tokens is None else tokens
+    slot = torch.empty((B, N), dtype=torch.int32, device=dev) if slot is None else slot
+    q = torch.empty((B, N, K), dtype=torch.float32, device=dev) if q is None else q
+    status = torch.empty((B,), dtype=torch.int32, device=dev) if status is None else status
+    if ws is None:
+        ws = workspace(select_workspace_bytes(B, N), dev)
+    rc = _lib.dflash2_select_q8(_ptr(cand_idx), _ptr(cand_val), _ptr(gate),
+                                *[_ptr(a) for a in pred_q8], *[_ptr(a) for a in succ_q8], V, R,
+                                _ptr(anchor), _ptr(temperature), int(seed) & (2**64 - 1),
+                                int(step) & (2**64 - 1), B, N, _ptr(tokens), _ptr(slot), _ptr(q),
+                                _ptr(status), _ptr(ws), ws.numel(), _stream(stream))
+    _check(rc, "dflash2_select_q8")
     return tokens, slot, q, status
 
 

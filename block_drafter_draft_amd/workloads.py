@@ -229,6 +229,28 @@ def codebooks(cfg: Config):
     return out[0], out[1]
 
 
+def q8_quantize(x: np.ndarray, group: int = 64):
+    """Affine Q8 of rows [V, R] in groups of `group`: bf16 scale and bias per group, then
+    codes in 0..255 chosen against the stored (bf16-rounded) scale and bias. Returns
+    (codes uint8 [V, R], scale bf16 bits [V, R/group], bias bf16 bits [V, R/group]).
+    This is input preparation (a converter's job), not part of the selector."""
+    V, R = x.shape
+    xg = x.astype(np.float32).reshape(V, R // group, group)
+    lo, hi = xg.min(axis=2), xg.max(axis=2)
+    scale = to_bf16_bits(np.maximum((hi - lo) / np.float32(255.0), np.float32(1e-8)))
+    bias = to_bf16_bits(lo)
+    s = bf16_bits_to_f32(scale)[..., None]
+    z = bf16_bits_to_f32(bias)[..., None]
+    codes = np.clip(np.rint((xg - z) / s), 0, 255).astype(np.uint8).reshape(V, R)
+    return codes, scale, bias
+
+
+def codebooks_q8(cfg: Config):
+    """The bf16 codebooks of `codebooks`, converted to affine Q8 (groups of 64)."""
+    A, Bc = codebooks(cfg)
+    return q8_quantize(bf16_bits_to_f32(A)), q8_quantize(bf16_bits_to_f32(Bc))
+
+
 def gate(cfg: Config, seqs=None, iset: int = 0) -> np.ndarray:
     return _per_seq(cfg, _T_GATE, 0, seqs, iset, (cfg.N, cfg.R), _normal)
 

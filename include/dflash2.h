@@ -212,6 +212,25 @@ int dflash2_select(const int32_t *cand_idx, const float *cand_val, const float *
 size_t dflash2_select_workspace_bytes(int B, int N);
 
 /*
+ * dflash2_select_q8 - dflash2_select over affine-Q8 codebooks ("Geramy/LSE docs/DFLASH2.md",
+ * conversion notes: selector codebooks in affine Q8 with groups of 64, BF16 scale and bias,
+ * FP32 activations and accumulation).
+ *   pred_codes, succ_codes [V, R] uint8; pred_scale, pred_bias, succ_scale, succ_bias
+ *   [V, R/64] bf16 bits. Element r of row v is fl(fl(scale[v, r/64] * code[v, r]) +
+ *   bias[v, r/64]) in binary32 (scale and bias widened from bf16); lattice, path, outputs
+ *   and status are those of dflash2_select with these values in place of the bf16 codebook
+ *   entries. Requires R % 64 == 0, R <= 512, 16-byte aligned codes and gate.
+ *   Workspace: dflash2_select_workspace_bytes.
+ */
+int dflash2_select_q8(const int32_t *cand_idx, const float *cand_val, const float *gate,
+                      const uint8_t *pred_codes, const uint16_t *pred_scale,
+                      const uint16_t *pred_bias, const uint8_t *succ_codes,
+                      const uint16_t *succ_scale, const uint16_t *succ_bias, int V, int R,
+                      const int32_t *anchor, const float *temperature, uint64_t seed,
+                      uint64_t step, int B, int N, int32_t *tokens, int32_t *slot, float *q,
+                      int32_t *status, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * dflash2_verify - target verification of the N proposals ("Geramy/LSE docs/DFLASH2.md",
  * usage and drafter-geometry paragraphs: probability-ratio rejection with residual
  * sampling, the target consumes the anchor plus all proposals, greedy keeps the

@@ -74,6 +74,10 @@ def lib():
                                  c_u64, c_u64, c_int, c_int, i32p, i32p, f32p, i32p, f32p])
         L.or_verify.argtypes = ([vp, c_int, c_i64, c_i64, c_int, i32p, i32p, f32p, i32p, f32p,
                                  c_u64, c_u64, c_int, c_int, i32p, i32p, i32p])
+        L.or_select_q8.argtypes = ([i32p, f32p, f32p] + [vp] * 6 +
+                                   [c_int, c_int, i32p, f32p, c_u64, c_u64, c_int, c_int,
+                                    i32p, i32p, f32p, i32p, f32p])
+        L.or_q8_dequant.argtypes = [vp, vp, vp, c_i64, c_int, f32p]
         _lib = L
     return _lib
 
@@ -205,6 +209,43 @@ def select(cand_idx, cand_val, gate, pred_cb, succ_cb, anchor, temperature, seed
     if want_lattice:
         return tokens, slot, q, status, lat
     return tokens, slot, q, status
+
+
+def select_q8(cand_idx, cand_val, gate, pred_q8, succ_q8, anchor, temperature, seed, step,
+              want_lattice=False):
+    """The selector over affine-Q8 codebooks; pred_q8 / succ_q8 are (codes [V, R] uint8,
+    scale [V, R/64] bf16 bits, bias [V, R/64] bf16 bits)."""
+    B, N, _ = cand_idx.shape
+    V, R = pred_q8[0].shape
+    ci = np.ascontiguousarray(cand_idx, dtype=np.int32)
+    cv = np.ascontiguousarray(cand_val, dtype=np.float32)
+    g = np.ascontiguousarray(gate, dtype=np.float32)
+    pa = [np.ascontiguousarray(a) for a in pred_q8]
+    sa = [np.ascontiguousarray(a) for a in succ_q8]
+    assert pa[0].dtype == np.uint8 and pa[1].dtype == np.uint16 and pa[2].dtype == np.uint16
+    an = np.ascontiguousarray(anchor, dtype=np.int32)
+    T = np.ascontiguousarray(temperature, dtype=np.float32)
+    tokens = np.zeros((B, N), np.int32)
+    slot = np.zeros((B, N), np.int32)
+    q = np.zeros((B, N, K), np.float32)
+    status = np.zeros(B, np.int32)
+    lat = np.zeros((B, N, K, K), np.float32) if want_lattice else None
+    lib().or_select_q8(_p(ci), _p(cv), _p(g), *[_p(a) for a in pa], *[_p(a) for a in sa], V, R,
+                       _p(an), _p(T), ctypes.c_uint64(seed), ctypes.c_uint64(step), B, N,
+                       _p(tokens), _p(slot), _p(q), _p(status), _p(lat))
+    if want_lattice:
+        return tokens, slot, q, status, lat
+    return tokens, slot, q, status
+
+
+def q8_dequant(codes, scale, bias) -> np.ndarray:
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    sc = np.ascontiguousarray(scale, dtype=np.uint16)
+    bi = np.ascontiguousarray(bias, dtype=np.uint16)
+    V, R = c.shape
+    out = np.zeros((V, R), np.float32)
+    lib().or_q8_dequant(_p(c), _p(sc), _p(bi), V, R, _p(out))
+    return out
 
 
 def verify(target, B, N, seq_stride, row_stride, V, tokens, cand_idx, q, slot, temperature,

@@ -342,14 +342,43 @@ static int or_mode(float T, float *invT, int32_t *st) {
 /* error bound of exactly this evaluation.                                               */
 /* ------------------------------------------------------------------------------------ */
 
-static float or_transition(const uint16_t *A_row, const float *g, const uint16_t *B_row, int R) {
+static float or_transition(const float *A_row, const float *g, const float *B_row, int R) {
   float t = 0.0f;
   for (int r = 0; r < R; ++r) {
-    float ag = or_bf16_to_f32(A_row[r]) * g[r];
-    float pr = ag * or_bf16_to_f32(B_row[r]);
+    float ag = A_row[r] * g[r];
+    float pr = ag * B_row[r];
     t = t + pr;
   }
   return t;
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Codebook rows. bf16 rows widen exactly. Affine Q8 rows ([LSE] conversion notes: matrix */
+/* weights and selector codebooks use affine Q8 with groups of 64, BF16 scale and bias,  */
+/* FP32 activations and accumulation): reading, an unsigned 8-bit code q per element and */
+/* value = fl(fl(scale * q) + bias) in binary32, scale and bias of the element's group   */
+/* of 64 widened from bf16.                                                               */
+/* ------------------------------------------------------------------------------------ */
+
+typedef struct {
+  const uint16_t *bf16;  /* [V, R] bf16 bits, or NULL for Q8 */
+  const uint8_t *codes;  /* [V, R] */
+  const uint16_t *scale; /* [V, R / 64] bf16 bits */
+  const uint16_t *bias;  /* [V, R / 64] bf16 bits */
+} or_codebook;
+
+static void or_row(const or_codebook *cb, int64_t v, int R, float *out) {
+  if (cb->bf16) {
+    for (int r = 0; r < R; ++r) out[r] = or_bf16_to_f32(cb->bf16[v * R + r]);
+    return;
+  }
+  const int G = R / 64;
+  for (int r = 0; r < R; ++r) {
+    const float sc = or_bf16_to_f32(cb->scale[v * G + r / 64]);
+    const float bi = or_bf16_to_f32(cb->bias[v * G + r / 64]);
+    const float sq = sc * (float)cb->codes[v * R + r];
+    out[r] = sq + bi;
+  }
 }
 
 /* ------------------------------------------------------------------------------------ */
@@ -451,11 +480,14 @@ void or_walk(int K, int N, const float *s1, const float *s, float invT, const fl
 /* [B,N,16,16] scores; slot 1 fills row 0 (the anchor) and leaves rows 1..15 zero.       */
 /* ------------------------------------------------------------------------------------ */
 
-void or_select(const int32_t *cand_idx, const float *cand_val, const float *gate,
-               const uint16_t *pred_cb, const uint16_t *succ_cb, int V, int R,
-               const int32_t *anchor, const float *temperature, uint64_t seed, uint64_t step, int B,
-               int N, int32_t *tokens, int32_t *slot, float *q, int32_t *status, float *lattice) {
+static void or_select_cb(const int32_t *cand_idx, const float *cand_val, const float *gate,
+                         const or_codebook *pred_cb, const or_codebook *succ_cb, int V, int R,
+                         const int32_t *anchor, const float *temperature, uint64_t seed,
+                         uint64_t step, int B, int N, int32_t *tokens, int32_t *slot, float *q,
+                         int32_t *status, float *lattice) {
   const int K = OR_K;
+  float *arow = (float *)malloc(sizeof(float) * (size_t)R);
+  float *brow = (float *)malloc(sizeof(float) * (size_t)R);
   float *s1 = (float *)malloc(sizeof(float) * K);
   float *s = (float *)malloc(sizeof(float) * (size_t)(N > 1 ? N - 1 : 1) * K * K);
   float *uni = (float *)malloc(sizeof(float) * (size_t)N);
@@ -479,7 +511,9 @@ void or_select(const int32_t *cand_idx, const float *cand_val, const float *gate
           int64_t p = (i == 1) ? anchor[b] : ci[(i - 2) * K + kp];
           for (int k = 0; k < K; ++k) {
             int64_t c = ci[(i - 1) * K + k];
-            float t = or_transition(pred_cb + p * R, g, succ_cb + c * R, R);
+            or_row(pred_cb, p, R, arow);
+            or_row(succ_cb, c, R, brow);
+            float t = or_transition(arow, g, brow, R);
             float sc = cv[(i - 1) * K + k] + t;
             if (!isfinite(sc) || !isfinite(cv[(i - 1) * K + k])) finite = 0;
             if (i == 1)
@@ -527,6 +561,36 @@ void or_select(const int32_t *cand_idx, const float *cand_val, const float *gate
   free(uni);
   free(path);
   free(qq);
+  free(arow);
+  free(brow);
+}
+
+void or_select(const int32_t *cand_idx, const float *cand_val, const float *gate,
+               const uint16_t *pred_cb, const uint16_t *succ_cb, int V, int R,
+               const int32_t *anchor, const float *temperature, uint64_t seed, uint64_t step, int B,
+               int N, int32_t *tokens, int32_t *slot, float *q, int32_t *status, float *lattice) {
+  or_codebook a = {pred_cb, NULL, NULL, NULL}, c = {succ_cb, NULL, NULL, NULL};
+  or_select_cb(cand_idx, cand_val, gate, &a, &c, V, R, anchor, temperature, seed, step, B, N,
+               tokens, slot, q, status, lattice);
+}
+
+void or_select_q8(const int32_t *cand_idx, const float *cand_val, const float *gate,
+                  const uint8_t *pred_codes, const uint16_t *pred_scale, const uint16_t *pred_bias,
+                  const uint8_t *succ_codes, const uint16_t *succ_scale, const uint16_t *succ_bias,
+                  int V, int R, const int32_t *anchor, const float *temperature, uint64_t seed,
+                  uint64_t step, int B, int N, int32_t *tokens, int32_t *slot, float *q,
+                  int32_t *status, float *lattice) {
+  or_codebook a = {NULL, pred_codes, pred_scale, pred_bias};
+  or_codebook c = {NULL, succ_codes, succ_scale, succ_bias};
+  or_select_cb(cand_idx, cand_val, gate, &a, &c, V, R, anchor, temperature, seed, step, B, N,
+               tokens, slot, q, status, lattice);
+}
+
+/* Q8 rows as binary32 (for tests that compare against the dequantized values). */
+void or_q8_dequant(const uint8_t *codes, const uint16_t *scale, const uint16_t *bias, int64_t V,
+                   int R, float *out) {
+  or_codebook cb = {NULL, codes, scale, bias};
+  for (int64_t v = 0; v < V; ++v) or_row(&cb, v, R, out + v * R);
 }
 
 /* ------------------------------------------------------------------------------------ */

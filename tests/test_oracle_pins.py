@@ -823,3 +823,55 @@ def test_ring_update_counts_and_reset(orc):
                                     np.zeros((3, S, 1, 1), np.float32), S, W)
     np.testing.assert_array_equal(L, [5, 9, 2])
     np.testing.assert_array_equal(st, [orc.ST_BADCOUNT, orc.ST_BADCOUNT, 0])
+
+
+# ----------------------------------------------------------------------------------------
+# Selector over affine-Q8 codebooks
+# ----------------------------------------------------------------------------------------
+
+def _exact_q8_rows(rng, V, R):
+    """Q8 codebooks whose values are exact in bf16: per-group power-of-two scales, small
+    integer-multiple biases and codes, with the equivalent bf16 rows built independently
+    (binary64 arithmetic, then an exact conversion)."""
+    G = R // 64
+    # value = (code + k) * scale with code + k in [-32, 255]: 8 significant bits at most
+    codes = rng.integers(0, 224, size=(V, R)).astype(np.uint8)
+    sc = np.float32(2.0) ** rng.integers(-7, -4, size=(V, G)).astype(np.float32)
+    bi = (rng.integers(-32, 33, size=(V, G)) * sc).astype(np.float32)
+    vals = codes.astype(np.float64) * np.repeat(sc, 64, axis=1) + np.repeat(bi, 64, axis=1)
+    bf = to_bf16_bits(vals.astype(np.float32))
+    assert np.array_equal(bf16_bits_to_f32(bf).astype(np.float64), vals)  # exact
+    return (codes, to_bf16_bits(sc), to_bf16_bits(bi)), bf
+
+
+@pytest.mark.parametrize("T", [0.0, 0.8])
+def test_select_q8_equals_bf16_select_on_exact_codebooks(orc, T):
+    # with every dequantized value exact in bf16, the Q8 selector must reproduce the bf16
+    # selector bit for bit (a wrong group, swapped scale/bias or a signed code would not)
+    rng = np.random.default_rng(85)
+    V, R, B, N = 500, 256, 3, 7
+    pq, pb = _exact_q8_rows(rng, V, R)
+    sq, sb = _exact_q8_rows(rng, V, R)
+    ci = np.stack([np.stack([rng.choice(V, 16, replace=False) for _ in range(N)])
+                   for _ in range(B)]).astype(np.int32)
+    cv = rng.standard_normal((B, N, 16)).astype(np.float32)
+    g = rng.standard_normal((B, N, R)).astype(np.float32)
+    an = rng.integers(0, V, size=B).astype(np.int32)
+    temp = np.full(B, T, np.float32)
+    a = orc.select_q8(ci, cv, g, pq, sq, an, temp, 5, 1, want_lattice=True)
+    b = orc.select(ci, cv, g, pb, sb, an, temp, 5, 1, want_lattice=True)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_q8_quantizer_error_bound(orc):
+    # the converter's convention (codes chosen against the stored bf16 scale and bias):
+    # every dequantized value lies within half a step (plus the bias rounding) of the input
+    rng = np.random.default_rng(86)
+    from block_drafter_draft_amd.workloads import q8_quantize
+    x = (rng.standard_normal((40, 256)) / 4).astype(np.float32)
+    codes, sc, bi = q8_quantize(x)
+    d = orc.q8_dequant(codes, sc, bi)
+    s = np.repeat(bf16_bits_to_f32(sc), 64, axis=1)
+    lo = np.repeat(np.abs(x.reshape(40, 4, 64)).max(axis=2), 64, axis=1)
+    assert np.all(np.abs(d - x) <= 0.5 * s + lo * 2.0 ** -8 + 1e-7)
