@@ -10,8 +10,8 @@ the working set exceeds the 256 MiB last-level cache. Each step is one HIP-graph
 Prints one JSON line: throughput, a roofline record for the block-attention call (its
 algorithmic bytes over its average duration, measured with HIP events on its stream), the
 CPU oracle timed on a bounded sample on one host core, and separate records for the
-output-head projection fused with the top-16 and for the selector over Q8 codebooks
-(neither is part of the step).
+output-head projection fused with the top-16, the selector over Q8 codebooks and the
+best-first draft tree (none of them part of the step).
 """
 from __future__ import annotations
 
@@ -125,7 +125,7 @@ def main():
     ap.add_argument("--no-lmhead", action="store_true",
                     help="skip the separate output-head projection + top-16 measurement")
     ap.add_argument("--no-q8", action="store_true",
-                    help="skip the separate selector-over-Q8-codebooks measurement")
+                    help="skip the separate Q8-selector and draft-tree measurements")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 1 GiB device copy (calibrates HBM byte counters)")
@@ -312,6 +312,22 @@ def main():
                      "bf16_select_us_per_call": stage_ms["select"] * 1e3}
         del pq_d, sq_d
 
+    # The best-first draft tree over the selector lattice (a call outside the step),
+    # budget 12 (the pages' tree budget), same candidates, gates and anchors.
+    ddtree = None
+    if not args.no_q8:
+        tree_out = None
+
+        def tree_call(r):
+            nonlocal tree_out
+            x = inputs[r % nsets]
+            tree_out = d2.ddtree(o.cand_idx, o.cand_val, x.gate, x.pred_cb, x.succ_cb, x.anchor,
+                                 12, out=tree_out, ws=runner.ws_sel)
+
+        tree_call(0)
+        torch.cuda.synchronize()
+        ddtree = {"call": "dflash2_ddtree", "budget": 12, "us_per_call": timed(tree_call, reps) * 1e3}
+
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -349,6 +365,7 @@ def main():
         "cpu_baseline": None,
         "lmhead_topk16": lmhead,
         "select_q8": select_q8,
+        "ddtree": ddtree,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")

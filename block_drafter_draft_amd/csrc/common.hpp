@@ -148,6 +148,34 @@ __device__ __forceinline__ float exp_c(float y) {
 }
 
 // ---------------------------------------------------------------------------------------
+// log_c(x), x > 0 finite: x = 2^e m with m in [sqrt(1/2), sqrt(2)); log x = e ln 2 +
+// 2 atanh(u), u = (m - 1) / (m + 1), with 2 atanh(u) = 2u (1 + u^2/3 + u^4/5 + u^6/7 +
+// u^8/9) in Horner form and e ln 2 split in two constants. Each step is one correctly
+// rounded binary32 operation, so every IEEE implementation of these steps agrees.
+// ---------------------------------------------------------------------------------------
+
+__device__ __forceinline__ float log_c(float x) {
+  const float kLn2Hi = 0.693145751953125f;
+  const float kLn2Lo = 1.42860677e-06f;
+  int e = 0;
+  float m = frexpf(x, &e);  // [0.5, 1), exact
+  if (m < 0.707106769f) {
+    m = __fmul_rn(m, 2.0f);
+    e -= 1;
+  }
+  const float u = __fdiv_rn(__fsub_rn(m, 1.0f), __fadd_rn(m, 1.0f));
+  const float u2 = __fmul_rn(u, u);
+  float p = 0.111111112f;
+  p = __fmaf_rn(p, u2, 0.142857149f);
+  p = __fmaf_rn(p, u2, 0.2f);
+  p = __fmaf_rn(p, u2, 0.333333343f);
+  p = __fmaf_rn(p, u2, 1.0f);
+  const float t = __fmul_rn(__fmul_rn(2.0f, u), p);
+  const float ef = (float)e;
+  return __fmaf_rn(ef, kLn2Hi, __fmaf_rn(ef, kLn2Lo, t));
+}
+
+// ---------------------------------------------------------------------------------------
 // Temperature classes: 0 greedy, 1 sampled; sets DFLASH2_ST_BADTEMP for invalid values.
 // ---------------------------------------------------------------------------------------
 

@@ -398,6 +398,173 @@ __global__ __launch_bounds__(64) void select_path_kernel(
   if (lane == 0) status[b] = st;
 }
 
+// Draft tree by best-first expansion over the lattice ("qwen35: DSpark speculative decoding
+// (Qwen3.8-27B drafters) - #625", the DDTree commit: candidates scored as draft log-prob
+// plus the selector's compatibility with the branch's actual parent, log-softmax
+// normalised per position, expanded best-first under a node budget). One wave per
+// sequence: the lattice rows are normalised (d = s - max, Z = sum exp_c(d) in k order,
+// ls = d - log_c(Z)), then each of `budget` rounds takes the frontier entry with the
+// largest score (ties: the earliest added) by one 64-bit wave maximum over packed
+// (score key, ~entry) words, records it, and appends its 16 children in k order.
+constexpr int kMaxBudget = 64;
+constexpr int kMaxFrontier = kTopK + kMaxBudget * kTopK;
+
+__global__ __launch_bounds__(64) void ddtree_kernel(
+    const int32_t* __restrict__ cidx, const float* __restrict__ cval, int V,
+    const int32_t* __restrict__ anchor, int N, int budget, const float* __restrict__ lattice,
+    int32_t* __restrict__ parent, int32_t* __restrict__ depth, int32_t* __restrict__ slotk,
+    int32_t* __restrict__ token, float* __restrict__ score, int32_t* __restrict__ status) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  __shared__ float LS[kMaxN][kTopK][kTopK];
+  __shared__ int32_t cid[kMaxN * kTopK];
+  __shared__ float fs[kMaxFrontier];
+  __shared__ uint32_t fmeta[kMaxFrontier];  // depth | k << 4 | (parent + 1) << 8 | alive << 16
+  __shared__ int32_t opar[kMaxBudget], odep[kMaxBudget], oslt[kMaxBudget], otok[kMaxBudget];
+  __shared__ float osc[kMaxBudget];
+
+  // every input load first (as in the path kernel), indices past the end clamped
+  constexpr int kPerLane = kMaxN * kTopK / 64 + 1;
+  constexpr int kLat4 = kMaxN * kTopK * kTopK / 4 / 64;
+  const int ncand = N * kTopK, nlat4 = N * kTopK * kTopK / 4;
+  const int32_t anc = anchor[b];
+  int32_t cl[kPerLane];
+  float vl[kPerLane];
+#pragma unroll
+  for (int u = 0; u < kPerLane; ++u) {
+    const int e = min(lane + 64 * u, ncand - 1);
+    cl[u] = cidx[(int64_t)b * ncand + e];
+    vl[u] = cval[(int64_t)b * ncand + e];
+  }
+  const float4* lat4 = reinterpret_cast<const float4*>(lattice + (int64_t)b * N * kTopK * kTopK);
+  float4 lv[kLat4];
+#pragma unroll
+  for (int u = 0; u < kLat4; ++u) lv[u] = lat4[min(lane + 64 * u, nlat4 - 1)];
+
+  int bad = !(anc >= 0 && anc < V);
+#pragma unroll
+  for (int u = 0; u < kPerLane; ++u) {
+    const int e = lane + 64 * u;
+    if (e < ncand) {
+      cid[e] = cl[u];
+      bad |= !(cl[u] >= 0 && cl[u] < V);
+    }
+  }
+  const bool ok = wave_or(bad) == 0;
+  int st = ok ? 0 : DFLASH2_ST_BADTOKEN;
+  int nonfin = 0;
+  if (ok) {
+    float* Sf = &LS[0][0][0];
+#pragma unroll
+    for (int u = 0; u < kLat4; ++u) {
+      const int e4 = lane + 64 * u;
+      if (e4 < nlat4) {
+        const float sv[4] = {lv[u].x, lv[u].y, lv[u].z, lv[u].w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const int e = 4 * e4 + h;
+          const int i = e / (kTopK * kTopK) + 1, kp = (e / kTopK) % kTopK;
+          Sf[e] = sv[h];
+          if (!(i == 1 && kp > 0)) nonfin |= !(fabsf(sv[h]) <= 3.40282347e38f);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPerLane; ++u)
+      if (lane + 64 * u < ncand) nonfin |= !(fabsf(vl[u]) <= 3.40282347e38f);
+  }
+  const bool finite = wave_or(nonfin) == 0;
+  if (ok && !finite) st |= DFLASH2_ST_NONFINITE;
+  const int64_t o = (int64_t)b * budget;
+  if (!ok || !finite) {
+    for (int t = lane; t < budget; t += 64) {
+      parent[o + t] = depth[o + t] = slotk[o + t] = token[o + t] = -1;
+      score[o + t] = 0.0f;
+    }
+    if (lane == 0) status[b] = st;
+    return;
+  }
+  __syncthreads();
+
+  // normalise every parent row: slot 1 has only the anchor's row
+  const int nrows = 1 + (N - 1) * kTopK;
+  for (int q = lane; q < nrows; q += 64) {
+    const int i = q == 0 ? 1 : 2 + (q - 1) / kTopK, kp = q == 0 ? 0 : (q - 1) % kTopK;
+    float* row = &LS[i - 1][kp][0];
+    float v[kTopK];
+#pragma unroll
+    for (int k = 0; k < kTopK; ++k) v[k] = row[k];
+    float m = v[0];
+#pragma unroll
+    for (int k = 1; k < kTopK; ++k) m = v[k] > m ? v[k] : m;
+    float Z = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kTopK; ++k) {
+      v[k] = __fsub_rn(v[k], m);
+      Z = __fadd_rn(Z, exp_c(v[k]));
+    }
+    const float lz = log_c(Z);
+#pragma unroll
+    for (int k = 0; k < kTopK; ++k) row[k] = __fsub_rn(v[k], lz);
+  }
+  __syncthreads();
+
+  if (lane < kTopK) {
+    fs[lane] = __fadd_rn(0.0f, LS[0][0][lane]);
+    fmeta[lane] = 1u | ((uint32_t)lane << 4) | (1u << 16);
+  }
+  int F = kTopK;
+  __syncthreads();
+  for (int t = 0; t < budget; ++t) {
+    uint64_t key = 0;
+    for (int f = lane; f < F; f += 64) {
+      if (fmeta[f] >> 16) {
+        const uint64_t w = ((uint64_t)KeyF32::canon(__float_as_uint(fs[f])) << 32) |
+                           (uint64_t)(~(uint32_t)f);
+        key = w > key ? w : key;
+      }
+    }
+    key = wave_max_u64(key);
+    if (key == 0) {  // the whole tree is taken
+      if (lane == 0) {
+        opar[t] = odep[t] = oslt[t] = otok[t] = -1;
+        osc[t] = 0.0f;
+      }
+      __syncthreads();
+      continue;
+    }
+    const int f = (int)(~(uint32_t)key);
+    const float sf = fs[f];
+    const uint32_t meta = fmeta[f];
+    const int dd = meta & 15u, kk = (meta >> 4) & 15u, pp = (int)((meta >> 8) & 255u) - 1;
+    __syncthreads();  // every lane has read the entry
+    if (lane == 0) {
+      fmeta[f] = meta & 0xffffu;  // taken
+      opar[t] = pp;
+      odep[t] = dd;
+      oslt[t] = kk;
+      otok[t] = cid[(dd - 1) * kTopK + kk];
+      osc[t] = sf;
+    }
+    if (dd < N) {
+      if (lane < kTopK) {
+        fs[F + lane] = __fadd_rn(sf, LS[dd][kk][lane]);
+        fmeta[F + lane] =
+            (uint32_t)(dd + 1) | ((uint32_t)lane << 4) | ((uint32_t)(t + 1) << 8) | (1u << 16);
+      }
+      F += kTopK;
+    }
+    __syncthreads();
+  }
+  for (int t = lane; t < budget; t += 64) {
+    parent[o + t] = opar[t];
+    depth[o + t] = odep[t];
+    slotk[o + t] = oslt[t];
+    token[o + t] = otok[t];
+    score[o + t] = osc[t];
+  }
+  if (lane == 0) status[b] = st;
+}
+
 }  // namespace
 }  // namespace df2
 
@@ -473,5 +640,40 @@ extern "C" int dflash2_select_q8(const int32_t* cand_idx, const float* cand_val,
         succ_bias, V, R, anchor, N, lattice);
   select_path_kernel<<<B, 64, 0, stream>>>(cand_idx, cand_val, V, anchor, temperature, seed, step,
                                            N, lattice, tokens, slot, q, status);
+  return launch_status();
+}
+
+extern "C" size_t dflash2_ddtree_workspace_bytes(int B, int N) {
+  return dflash2_select_workspace_bytes(B, N);
+}
+
+extern "C" int dflash2_ddtree(const int32_t* cand_idx, const float* cand_val, const float* gate,
+                              const uint16_t* pred_cb, const uint16_t* succ_cb, int V, int R,
+                              const int32_t* anchor, int B, int N, int budget, int32_t* parent,
+                              int32_t* depth, int32_t* slot, int32_t* token, float* score,
+                              int32_t* status, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!cand_idx || !cand_val || !gate || !pred_cb || !succ_cb || !anchor || !parent || !depth ||
+      !slot || !token || !score || !status || !ws)
+    return DFLASH2_EINVAL;
+  if (B < 1 || N < 1 || R < 1 || V < kTopK || budget < 1) return DFLASH2_EINVAL;
+  if (N > kMaxN || R > kMaxR || B > 65535 || budget > kMaxBudget) return DFLASH2_EUNSUPPORTED;
+  if (!aligned(ws, kWsAlign) || ws_bytes < dflash2_ddtree_workspace_bytes(B, N))
+    return DFLASH2_EWORKSPACE;
+  float* lattice = (float*)ws;
+  const int RS = lat_row_stride(R);
+  const size_t lds = (size_t)2 * kTopK * RS * sizeof(uint16_t) + (size_t)RS * sizeof(float) +
+                     (size_t)kTopK * RS * sizeof(float);
+  const bool vec = R % 8 == 0 && aligned(pred_cb, 16) && aligned(succ_cb, 16) && aligned(gate, 16);
+  if (vec && R <= 256)
+    select_lattice_kernel<true, 4><<<dim3(N, B), 256, lds, stream>>>(
+        cand_idx, cand_val, gate, pred_cb, succ_cb, V, R, anchor, N, lattice);
+  else if (vec)
+    select_lattice_kernel<true, 8><<<dim3(N, B), 256, lds, stream>>>(
+        cand_idx, cand_val, gate, pred_cb, succ_cb, V, R, anchor, N, lattice);
+  else
+    select_lattice_kernel<false, 1><<<dim3(N, B), 256, lds, stream>>>(
+        cand_idx, cand_val, gate, pred_cb, succ_cb, V, R, anchor, N, lattice);
+  ddtree_kernel<<<B, 64, 0, stream>>>(cand_idx, cand_val, V, anchor, N, budget, lattice, parent,
+                                      depth, slot, token, score, status);
   return launch_status();
 }

@@ -48,6 +48,8 @@ SIGNATURES = {
     "dflash2_lmhead_topk16_workspace_bytes": ([_i32] * 4, _sz),
     "dflash2_select": ([_vp] * 5 + [_i32, _i32, _vp, _vp, _u64, _u64, _i32, _i32] + [_vp] * 5 + [_sz, _vp], _i32),
     "dflash2_select_workspace_bytes": ([_i32] * 2, _sz),
+    "dflash2_ddtree": ([_vp] * 5 + [_i32, _i32, _vp, _i32, _i32, _i32] + [_vp] * 7 + [_sz, _vp], _i32),
+    "dflash2_ddtree_workspace_bytes": ([_i32] * 2, _sz),
     "dflash2_select_q8": ([_vp] * 9 + [_i32, _i32, _vp, _vp, _u64, _u64, _i32, _i32] + [_vp] * 5 + [_sz, _vp], _i32),
     "dflash2_verify": ([_vp, _i32, _i64, _i64, _i32] + [_vp] * 5 + [_u64, _u64, _i32, _i32] + [_vp] * 4 + [_sz, _vp], _i32),
     "dflash2_verify_workspace_bytes": ([_i32] * 4, _sz),
@@ -241,6 +243,29 @@ def select(cand_idx, cand_val, gate, pred_cb, succ_cb, anchor, temperature, seed
                              ws.numel(), _stream(stream))
     _check(rc, "dflash2_select")
     return tokens, slot, q, status
+
+
+def ddtree(cand_idx, cand_val, gate, pred_cb, succ_cb, anchor, budget, out=None, ws=None,
+           stream=None):
+    """Best-first draft tree; returns (parent, depth, slot, token, score, status)."""
+    _dev(cand_idx, cand_val, gate, pred_cb, succ_cb, anchor)
+    _contig(cand_idx, cand_val, gate, pred_cb, succ_cb, anchor)
+    B, N, _ = cand_idx.shape
+    V, R = pred_cb.shape
+    if pred_cb.dtype != torch.bfloat16 or succ_cb.dtype != torch.bfloat16:
+        raise TypeError("codebooks must be bfloat16")
+    dev = cand_idx.device
+    if out is None:
+        out = tuple(torch.empty((B, budget), dtype=torch.int32, device=dev) for _ in range(4)) + (
+            torch.empty((B, budget), dtype=torch.float32, device=dev),
+            torch.empty((B,), dtype=torch.int32, device=dev))
+    if ws is None:
+        ws = workspace(int(_lib.dflash2_ddtree_workspace_bytes(B, N)), dev)
+    rc = _lib.dflash2_ddtree(_ptr(cand_idx), _ptr(cand_val), _ptr(gate), _ptr(pred_cb),
+                             _ptr(succ_cb), V, R, _ptr(anchor), B, N, budget,
+                             *[_ptr(t) for t in out], _ptr(ws), ws.numel(), _stream(stream))
+    _check(rc, "dflash2_ddtree")
+    return out
 
 
 def select_q8(cand_idx, cand_val, gate, pred_q8, succ_q8, anchor, temperature, seed, step,

@@ -212,6 +212,31 @@ int dflash2_select(const int32_t *cand_idx, const float *cand_val, const float *
 size_t dflash2_select_workspace_bytes(int B, int N);
 
 /*
+ * dflash2_ddtree - a draft tree by best-first expansion over the selector lattice ("qwen35:
+ * DSpark speculative decoding (Qwen3.8-27B drafters) - #625", the DDTree commit: candidates
+ * scored as draft log-probability plus the selector's compatibility with the branch's actual
+ * parent, log-softmax normalised per position, expanded best-first under a node budget).
+ *   Inputs as dflash2_select (no temperature: the tree is deterministic). The edge score
+ *   is the selector lattice s_i(p, k); for each parent row d_k = fl(s_k - max),
+ *   Z = sum_k exp_c(d_k) (k ascending), ls_k = fl(d_k - log_c(Z)) (log_c: a fixed binary32
+ *   log by exponent split and a degree-9 odd atanh series). A node's score is fl(parent
+ *   score + ls), the root (the anchor) scoring 0. The frontier starts with the root's 16
+ *   children (k order); each of `budget` rounds takes the entry with the largest score
+ *   (ties: the earliest added), records it and, below depth N, adds its 16 children.
+ *   parent, depth, slot, token [B, budget] int32 and score [B, budget] f32, in the order
+ *   taken: parent is the tree index of the node's parent (-1 under the root), depth 1..N,
+ *   slot the candidate index k, token cand_idx[b, depth-1, k]. Index and finiteness
+ *   problems set ST_BADTOKEN / ST_NONFINITE as in dflash2_select (outputs -1, score 0);
+ *   status is written. Requires 1 <= budget <= 64. Workspace: dflash2_ddtree_workspace_bytes.
+ */
+int dflash2_ddtree(const int32_t *cand_idx, const float *cand_val, const float *gate,
+                   const uint16_t *pred_cb, const uint16_t *succ_cb, int V, int R,
+                   const int32_t *anchor, int B, int N, int budget, int32_t *parent,
+                   int32_t *depth, int32_t *slot, int32_t *token, float *score, int32_t *status,
+                   void *ws, size_t ws_bytes, hipStream_t stream);
+size_t dflash2_ddtree_workspace_bytes(int B, int N);
+
+/*
  * dflash2_select_q8 - dflash2_select over affine-Q8 codebooks ("Geramy/LSE docs/DFLASH2.md",
  * conversion notes: selector codebooks in affine Q8 with groups of 64, BF16 scale and bias,
  * FP32 activations and accumulation).

@@ -78,6 +78,11 @@ def lib():
                                    [c_int, c_int, i32p, f32p, c_u64, c_u64, c_int, c_int,
                                     i32p, i32p, f32p, i32p, f32p])
         L.or_q8_dequant.argtypes = [vp, vp, vp, c_i64, c_int, f32p]
+        L.or_log_c.argtypes = [c_f32]
+        L.or_log_c.restype = c_f32
+        L.or_log_c_many.argtypes = [f32p, f32p, c_i64]
+        L.or_ddtree.argtypes = ([i32p, f32p, f32p, u16p, u16p, c_int, c_int, i32p, c_int, c_int,
+                                 c_int, i32p, i32p, i32p, i32p, f32p, i32p])
         _lib = L
     return _lib
 
@@ -357,3 +362,36 @@ def ring_update(new_k, new_v, n_new, back, ctx_len, k_ring, v_ring, S, W, status
             vr[b, (Lr + j) % S] = new_v[b, j]
         L[b] = Lr + n
     return L, kr, vr, st
+
+
+def log_c(x: float) -> float:
+    return float(lib().or_log_c(ctypes.c_float(x)))
+
+
+def log_c_array(x: np.ndarray) -> np.ndarray:
+    xs = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.zeros_like(xs)
+    lib().or_log_c_many(_p(xs), _p(out), xs.size)
+    return out
+
+
+def ddtree(cand_idx, cand_val, gate, pred_cb, succ_cb, anchor, budget):
+    """Best-first draft tree over the selector lattice; returns (parent, depth, slot, token,
+    score, status), the first five [B, budget]."""
+    B, N, _ = cand_idx.shape
+    V, R = pred_cb.shape
+    ci = np.ascontiguousarray(cand_idx, dtype=np.int32)
+    cv = np.ascontiguousarray(cand_val, dtype=np.float32)
+    g = np.ascontiguousarray(gate, dtype=np.float32)
+    A = np.ascontiguousarray(pred_cb, dtype=np.uint16)
+    Bc = np.ascontiguousarray(succ_cb, dtype=np.uint16)
+    an = np.ascontiguousarray(anchor, dtype=np.int32)
+    par = np.zeros((B, budget), np.int32)
+    dep = np.zeros((B, budget), np.int32)
+    slt = np.zeros((B, budget), np.int32)
+    tok = np.zeros((B, budget), np.int32)
+    sc = np.zeros((B, budget), np.float32)
+    st = np.zeros(B, np.int32)
+    lib().or_ddtree(_p(ci), _p(cv), _p(g), _p(A), _p(Bc), V, R, _p(an), B, N, budget, _p(par),
+                    _p(dep), _p(slt), _p(tok), _p(sc), _p(st))
+    return par, dep, slt, tok, sc, st

@@ -586,6 +586,134 @@ void or_select_q8(const int32_t *cand_idx, const float *cand_val, const float *g
                tokens, slot, q, status, lattice);
 }
 
+/* ------------------------------------------------------------------------------------ */
+/* Draft tree by best-first expansion over the selector lattice ("qwen35: DSpark          */
+/* speculative decoding (Qwen3.8-27B drafters) - #625", the DDTree commit: each expansion */
+/* scores a candidate as its draft log-probability plus the selector's compatibility with */
+/* the branch's actual parent, log-softmax normalised per position so that cumulative     */
+/* best-first comparisons across depths stay on one scale, under a node budget).          */
+/* Readings: the edge score is the selector lattice s_i(p, k) (candidate value plus the   */
+/* rank-R term); for each parent row, d_k = fl(s_k - max), Z = sum_k exp_c(d_k) (k        */
+/* ascending), ls_k = fl(d_k - log_c(Z)). A node is (depth i, candidate k, parent node);  */
+/* its score is fl(parent score + ls), the root (the anchor) scoring 0. The frontier       */
+/* starts with the root's 16 children (in k order); each of `budget` rounds takes the     */
+/* frontier entry with the largest score (ties: the earliest added), records it, and if   */
+/* its depth is below N adds its 16 children in k order. Outputs per tree node t (the      */
+/* order taken): parent (tree index, -1 under the root), depth (1..N), slot k, token and   */
+/* score. Index and finiteness checks are the selector's (BADTOKEN, NONFINITE; outputs -1 */
+/* and score 0).                                                                           */
+/* ------------------------------------------------------------------------------------ */
+
+float or_log_c(float x);
+
+void or_ddtree(const int32_t *cand_idx, const float *cand_val, const float *gate,
+               const uint16_t *pred_cb, const uint16_t *succ_cb, int V, int R,
+               const int32_t *anchor, int B, int N, int budget, int32_t *parent, int32_t *depth,
+               int32_t *slotk, int32_t *token, float *score, int32_t *status) {
+  const int K = OR_K;
+  or_codebook pa = {pred_cb, NULL, NULL, NULL}, pc = {succ_cb, NULL, NULL, NULL};
+  float *arow = (float *)malloc(sizeof(float) * (size_t)R);
+  float *brow = (float *)malloc(sizeof(float) * (size_t)R);
+  float *ls = (float *)malloc(sizeof(float) * (size_t)N * K * K);
+  const int fmax = K + budget * K;
+  float *fs = (float *)malloc(sizeof(float) * (size_t)fmax);
+  int *fd = (int *)malloc(sizeof(int) * (size_t)fmax);
+  int *fk = (int *)malloc(sizeof(int) * (size_t)fmax);
+  int *fp = (int *)malloc(sizeof(int) * (size_t)fmax);
+  int *alive = (int *)malloc(sizeof(int) * (size_t)fmax);
+  for (int b = 0; b < B; ++b) {
+    int32_t st = 0;
+    const int32_t *ci = cand_idx + (int64_t)b * N * K;
+    const float *cv = cand_val + (int64_t)b * N * K;
+    int ok = anchor[b] >= 0 && anchor[b] < V;
+    for (int e = 0; e < N * K; ++e)
+      if (ci[e] < 0 || ci[e] >= V) ok = 0;
+    int finite = 1;
+    if (ok) {
+      for (int i = 1; i <= N; ++i) {
+        const float *g = gate + ((int64_t)b * N + (i - 1)) * R;
+        const int npred = (i == 1) ? 1 : K;
+        for (int kp = 0; kp < npred; ++kp) {
+          const int64_t p = (i == 1) ? anchor[b] : ci[(i - 2) * K + kp];
+          float row[OR_K];
+          for (int k = 0; k < K; ++k) {
+            or_row(&pa, p, R, arow);
+            or_row(&pc, ci[(i - 1) * K + k], R, brow);
+            row[k] = cv[(i - 1) * K + k] + or_transition(arow, g, brow, R);
+            if (!isfinite(row[k]) || !isfinite(cv[(i - 1) * K + k])) finite = 0;
+          }
+          float m = row[0];
+          for (int k = 1; k < K; ++k) m = row[k] > m ? row[k] : m;
+          float d[OR_K], Z = 0.0f;
+          for (int k = 0; k < K; ++k) {
+            d[k] = row[k] - m;
+            Z = Z + or_exp_c(d[k]);
+          }
+          const float lz = or_log_c(Z);
+          for (int k = 0; k < K; ++k) ls[((int64_t)(i - 1) * K + kp) * K + k] = d[k] - lz;
+        }
+      }
+    }
+    if (!ok) st |= OR_ST_BADTOKEN;
+    if (ok && !finite) st |= OR_ST_NONFINITE;
+    int32_t *opar = parent + (int64_t)b * budget, *odep = depth + (int64_t)b * budget;
+    int32_t *oslt = slotk + (int64_t)b * budget, *otok = token + (int64_t)b * budget;
+    float *osc = score + (int64_t)b * budget;
+    if (!ok || !finite) {
+      for (int t = 0; t < budget; ++t) {
+        opar[t] = odep[t] = oslt[t] = otok[t] = -1;
+        osc[t] = 0.0f;
+      }
+      status[b] = st;
+      continue;
+    }
+    int F = 0;
+    for (int k = 0; k < K; ++k) {
+      fs[F] = 0.0f + ls[k]; /* slot 1, the anchor's row */
+      fd[F] = 1;
+      fk[F] = k;
+      fp[F] = -1;
+      alive[F] = 1;
+      ++F;
+    }
+    for (int t = 0; t < budget; ++t) {
+      int best = -1;
+      for (int f = 0; f < F; ++f)
+        if (alive[f] && (best < 0 || fs[f] > fs[best])) best = f;
+      if (best < 0) { /* nothing left (the whole tree is taken) */
+        opar[t] = odep[t] = oslt[t] = otok[t] = -1;
+        osc[t] = 0.0f;
+        continue;
+      }
+      alive[best] = 0;
+      opar[t] = fp[best];
+      odep[t] = fd[best];
+      oslt[t] = fk[best];
+      otok[t] = ci[(fd[best] - 1) * K + fk[best]];
+      osc[t] = fs[best];
+      if (fd[best] < N) {
+        for (int k = 0; k < K; ++k) {
+          fs[F] = fs[best] + ls[((int64_t)fd[best] * K + fk[best]) * K + k];
+          fd[F] = fd[best] + 1;
+          fk[F] = k;
+          fp[F] = t;
+          alive[F] = 1;
+          ++F;
+        }
+      }
+    }
+    status[b] = st;
+  }
+  free(arow);
+  free(brow);
+  free(ls);
+  free(fs);
+  free(fd);
+  free(fk);
+  free(fp);
+  free(alive);
+}
+
 /* Q8 rows as binary32 (for tests that compare against the dequantized values). */
 void or_q8_dequant(const uint8_t *codes, const uint16_t *scale, const uint16_t *bias, int64_t V,
                    int R, float *out) {
@@ -758,6 +886,39 @@ void or_verify(const void *target, int dtype, int64_t seq_stride, int64_t row_st
     n_accept[b] = n;
     status[b] |= st;
   }
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* log_c(x), x > 0 finite: x = 2^e * m with m in [sqrt(1/2), sqrt(2)), and               */
+/* log x = e ln 2 + 2 atanh(u), u = (m - 1) / (m + 1), |u| <= 0.1716, with               */
+/* 2 atanh(u) = 2u (1 + u^2/3 + u^4/5 + u^6/7 + u^8/9) in Horner form (fmaf) and e ln 2   */
+/* as e * LN2_HI + e * LN2_LO. Every step one correctly rounded binary32 operation.       */
+/* ------------------------------------------------------------------------------------ */
+
+float or_log_c(float x) {
+  const float LN2_HI = 0.693145751953125f;
+  const float LN2_LO = 1.42860677e-06f;
+  int e = 0;
+  float m = frexpf(x, &e); /* m in [0.5, 1), exact */
+  if (m < 0.707106769f) {
+    m = m * 2.0f;
+    e -= 1;
+  }
+  const float u = (m - 1.0f) / (m + 1.0f);
+  const float u2 = u * u;
+  float p = 0.111111112f;
+  p = fmaf(p, u2, 0.142857149f);
+  p = fmaf(p, u2, 0.2f);
+  p = fmaf(p, u2, 0.333333343f);
+  p = fmaf(p, u2, 1.0f);
+  const float t = (2.0f * u) * p;
+  const float ef = (float)e;
+  return fmaf(ef, LN2_HI, fmaf(ef, LN2_LO, t));
+}
+
+/* Vector form of or_log_c for the accuracy sweep in the tests. */
+void or_log_c_many(const float *x, float *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = or_log_c(x[i]);
 }
 
 /* Vector form of or_exp_c for the accuracy sweep in the tests. */

@@ -875,3 +875,72 @@ def test_q8_quantizer_error_bound(orc):
     s = np.repeat(bf16_bits_to_f32(sc), 64, axis=1)
     lo = np.repeat(np.abs(x.reshape(40, 4, 64)).max(axis=2), 64, axis=1)
     assert np.all(np.abs(d - x) <= 0.5 * s + lo * 2.0 ** -8 + 1e-7)
+
+
+# ----------------------------------------------------------------------------------------
+# log_c and the best-first draft tree
+# ----------------------------------------------------------------------------------------
+
+def test_log_c_accuracy(orc):
+    # within 3 ulp of binary64 log over [1, 16] (the normaliser's range) and a wide sweep;
+    # exactly 0 at 1, monotone on [1, 16]
+    x = np.concatenate([np.linspace(1, 16, 200001), np.geomspace(1e-30, 1e30, 40001)]).astype(np.float32)
+    got = orc.log_c_array(x).astype(np.float64)
+    ref = np.log(x.astype(np.float64))
+    ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(got - ref) <= 3 * np.maximum(ulp, 1e-45))
+    assert orc.log_c(1.0) == 0.0
+    seg = got[:200001]
+    assert np.all(np.diff(seg) >= 0)
+
+
+def _tree_inputs(rng, V=400, R=64, B=2, N=3):
+    A = to_bf16_bits(rng.standard_normal((V, R)).astype(np.float32) / 4)
+    Bc = to_bf16_bits(rng.standard_normal((V, R)).astype(np.float32) / 4)
+    ci = np.stack([np.stack([rng.choice(V, 16, replace=False) for _ in range(N)])
+                   for _ in range(B)]).astype(np.int32)
+    cv = (rng.standard_normal((B, N, 16)) * 1.5).astype(np.float32)
+    g = rng.standard_normal((B, N, R)).astype(np.float32)
+    an = rng.integers(0, V, size=B).astype(np.int32)
+    return ci, cv, g, A, Bc, an
+
+
+@pytest.mark.parametrize("budget", [1, 5, 17, 40])
+def test_ddtree_is_the_top_budget_nodes(orc, budget):
+    # Independent formulation: every node of the full tree (16 + 256 + 4096 at N = 3) with
+    # its cumulative binary64 log-softmax score over the selector lattice; best-first with
+    # a budget takes exactly the `budget` best nodes (scores only fall along a path), in
+    # descending order, each with its own parent.
+    rng = np.random.default_rng(87 + budget)
+    ci, cv, g, A, Bc, an = _tree_inputs(rng)
+    B, N = ci.shape[:2]
+    par, dep, slt, tok, sc, st = orc.ddtree(ci, cv, g, A, Bc, an, budget)
+    _, _, _, _, lat = orc.select(ci, cv, g, A, Bc, an, np.zeros(B, np.float32), 1, 0,
+                                 want_lattice=True)
+    for b in range(B):
+        def ls(i, kp):   # binary64 log-softmax of lattice row kp of slot i
+            row = lat[b, i - 1, kp].astype(np.float64)
+            m = row.max()
+            return row - m - np.log(np.exp(row - m).sum())
+        nodes = []       # (score, path)
+        frontier = [(0.0, ())]
+        for i in range(1, N + 1):
+            nxt = []
+            for s0, path in frontier:
+                kp = path[-1] if path else 0
+                l = ls(i, kp)
+                for k in range(16):
+                    nxt.append((s0 + l[k], path + (k,)))
+            nodes += nxt
+            frontier = nxt
+        nodes.sort(key=lambda z: -z[0])
+        want = nodes[:budget]
+        taken = {}
+        for t in range(budget):
+            path = want[t][1]
+            assert dep[b, t] == len(path) and slt[b, t] == path[-1]
+            assert par[b, t] == (taken[path[:-1]] if len(path) > 1 else -1)
+            assert tok[b, t] == ci[b, len(path) - 1, path[-1]]
+            assert abs(sc[b, t] - want[t][0]) < 1e-4
+            taken[path] = t
+    assert not st.any()
