@@ -255,6 +255,209 @@ __global__ __launch_bounds__(64 * kLmWaves) void lmhead_stream_kernel(
   }
 }
 
+// More than 32 hidden rows: the workgroup's four waves run in lockstep over the same
+// 64-column chunks of four neighbouring vocabulary blocks (one per wave, 32 rows each),
+// and share a tile of 128 hidden rows x 64 columns that the four waves copy into LDS
+// together (a quarter each). Per chunk a wave does 4 k-steps x 4 column blocks = 16
+// MFMA into four accumulators. Head and hidden tiles go through rings of four LDS
+// buffers, three chunks in flight: chunk i + 3 is issued after the barrier that follows
+// chunk i's wait, into the buffers chunk i - 1 used (every wave has finished it by then).
+// 16-byte chunks of the 128-byte LDS rows are XOR-swizzled by (row / 2) % 8, so both
+// operands' reads hit distinct banks. Each lane keeps four sorted lists (one per column
+// block); at the end the workgroup merges them as in the small kernel.
+constexpr int kTlCols = 128;                   // hidden rows per pass
+constexpr int kTlChunk = 64;                   // columns per chunk
+constexpr int kTlBufs = 4;
+constexpr int kTlW = kLmRows * kTlChunk;       // head tile, bf16 elements (4 KiB)
+constexpr int kTlH = kTlCols * kTlChunk;       // hidden tile, bf16 elements (16 KiB)
+constexpr int kTlNB = kTlCols / kLmCols;       // column blocks per wave (4)
+
+__device__ __forceinline__ int tl_swz(int r) { return (r >> 1) & 7; }
+
+struct TiledSmem {
+  union {
+    struct {
+      uint16_t w[kLmWaves][kTlBufs][kTlW];
+      uint16_t h[kTlBufs][kTlH];
+    } ring;
+    uint64_t lists[kLmWaves][kTlCols][kTopK];  // 64 KiB, for the final merge
+  };
+};
+
+__global__ __launch_bounds__(64 * kLmWaves) void lmhead_tiled_kernel(
+    const uint16_t* __restrict__ hid, int64_t hss, int64_t hrs, int row0, int N, int M,
+    const uint16_t* __restrict__ wt, int C, int V, int ngroups, uint64_t* __restrict__ lists) {
+  __shared__ TiledSmem sm;
+  const int t = threadIdx.x, lane = t & 63, n = lane & 31, hh = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int nwg = gridDim.x;
+  const int nblocks = (V + kLmRows - 1) / kLmRows;
+  const int nch = C / kTlChunk;
+  // block group g (four neighbouring blocks) of workgroup x is x + g * nwg
+  const int mygroups = blockIdx.x < ngroups ? (ngroups - 1 - blockIdx.x) / nwg + 1 : 0;
+  const int items = mygroups * nch;
+  const int mbase = blockIdx.y * kTlCols;
+
+  // this wave's share of the hidden tile: rows 32w + 8q + lane/8, q < 4 (clamped to M - 1)
+  const int lrow = lane >> 3;
+  const uint16_t* hsrc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = 32 * w + 8 * q + lrow;
+    int mr = mbase + r;
+    mr = mr < M ? mr : M - 1;
+    hsrc[q] = hid + (int64_t)(mr / N) * hss + (int64_t)(row0 + mr % N) * hrs +
+              8 * ((lane & 7) ^ tl_swz(r));
+  }
+  auto issue = [&](int item, int slot) {
+    item = item < items ? item : items - 1;  // past the end: a copy of the last one, unused
+    const int g = item / nch, k = item - g * nch;
+    const int blk = 4 * (blockIdx.x + g * nwg) + w;
+    const int v0 = blk * kLmRows;
+    const int c0 = k * kTlChunk;
+    uint16_t* dw = &sm.ring.w[w][slot][0];
+    uint16_t* dh = &sm.ring.h[slot][(32 * w) * kTlChunk];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 8 * q + lrow;
+      const int v = v0 + r < V ? v0 + r : V - 1;
+      const uint16_t* src = wt + (int64_t)v * C + c0 + 8 * ((lane & 7) ^ tl_swz(r));
+      __builtin_amdgcn_global_load_lds((const void*)src, DF2_LDS(dw + q * 512), 16, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(hsrc[q] + c0), DF2_LDS(dh + q * 512), 16,
+                                       0, 0);
+  };
+
+  uint64_t lst[kTlNB][kTopK];
+#pragma unroll
+  for (int nb = 0; nb < kTlNB; ++nb)
+#pragma unroll
+    for (int e = 0; e < kTopK; ++e) lst[nb][e] = 0;
+  f32x16_t acc[kTlNB];
+#pragma unroll
+  for (int nb = 0; nb < kTlNB; ++nb) acc[nb] = f32x16_t{};
+  const int swn = tl_swz(n);
+
+  auto compute = [&](int item, int slot) {
+    const int g = item / nch, k = item - g * nch;
+    const uint16_t* tw = &sm.ring.w[w][slot][0];
+    const uint16_t* th = &sm.ring.h[slot][0];
+#pragma unroll
+    for (int ks = 0; ks < kTlChunk / 16; ++ks) {
+      const int ch = 8 * ((2 * ks + hh) ^ swn);
+      const u32x4_t a = *reinterpret_cast<const u32x4_t*>(tw + n * kTlChunk + ch);
+#pragma unroll
+      for (int nb = 0; nb < kTlNB; ++nb) {
+        const u32x4_t bop =
+            *reinterpret_cast<const u32x4_t*>(th + (nb * kLmCols + n) * kTlChunk + ch);
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                          __builtin_bit_cast(bf16x8_t, bop),
+                                                          acc[nb], 0, 0, 0);
+      }
+    }
+    if (k == nch - 1) {
+      const int v0 = (4 * (blockIdx.x + g * nwg) + w) * kLmRows;
+#pragma unroll
+      for (int nb = 0; nb < kTlNB; ++nb) {
+        const bool mvalid = mbase + nb * kLmCols + n < M;
+        uint64_t cand[16], cmax = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int v = v0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+          cand[i] = mvalid && v < V ? pack_cand(KeyF32::canon(__float_as_uint(acc[nb][i])),
+                                                (uint32_t)v)
+                                    : 0ull;
+          cmax = cand[i] > cmax ? cand[i] : cmax;
+        }
+        if (__ballot(cmax > lst[nb][kTopK - 1])) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            uint64_t c = cand[i];
+            if (__ballot(c > lst[nb][kTopK - 1])) {
+#pragma unroll
+              for (int e = 0; e < kTopK; ++e) {
+                const uint64_t hi = lst[nb][e] > c ? lst[nb][e] : c;
+                c = lst[nb][e] > c ? c : lst[nb][e];
+                lst[nb][e] = hi;
+              }
+            }
+          }
+        }
+        acc[nb] = f32x16_t{};
+      }
+    }
+  };
+
+  if (items > 0) {
+    issue(0, 0);
+    issue(1, 1);
+    issue(2, 2);
+    for (int i = 0; i < items; ++i) {
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // chunk i's 8 copies have landed
+      __builtin_amdgcn_s_barrier();                         // ... everyone's, and i - 1 is done
+      issue(i + 3, (i + 3) & (kTlBufs - 1));
+      compute(i, i & (kTlBufs - 1));
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+
+  // one list per workgroup and hidden row (half-waves, then waves, by bitonic merges)
+#pragma unroll
+  for (int nb = 0; nb < kTlNB; ++nb) {
+    uint64_t o[kTopK];
+#pragma unroll
+    for (int e = 0; e < kTopK; ++e) {
+      const uint32_t lo = __shfl_xor((uint32_t)lst[nb][e], 32, 64);
+      const uint32_t hi = __shfl_xor((uint32_t)(lst[nb][e] >> 32), 32, 64);
+      o[e] = ((uint64_t)hi << 32) | lo;
+    }
+    merge_top16(lst[nb], o);
+  }
+  __syncthreads();  // every wave is done with the rings
+  auto put = [&]() {
+    if (hh == 0)
+#pragma unroll
+      for (int nb = 0; nb < kTlNB; ++nb)
+#pragma unroll
+        for (int e = 0; e < kTopK; ++e) sm.lists[w][nb * kLmCols + n][e] = lst[nb][e];
+  };
+  auto take = [&](int from) {
+#pragma unroll
+    for (int nb = 0; nb < kTlNB; ++nb) {
+      uint64_t o[kTopK];
+#pragma unroll
+      for (int e = 0; e < kTopK; ++e) o[e] = sm.lists[from][nb * kLmCols + n][e];
+      merge_top16(lst[nb], o);
+    }
+  };
+  put();
+  __syncthreads();
+  if ((w & 1) == 0) {
+    take(w + 1);
+    put();
+  }
+  __syncthreads();
+  if (w == 0) {
+    take(2);
+    if (hh == 0) {
+#pragma unroll
+      for (int nb = 0; nb < kTlNB; ++nb) {
+        const int m = mbase + nb * kLmCols + n;
+        if (m < M) {
+          uint64_t* out = lists + ((int64_t)m * gridDim.x + blockIdx.x) * kTopK;
+#pragma unroll
+          for (int e = 0; e < kTopK; e += 2)
+            *reinterpret_cast<u32x4_t*>(out + e) =
+                u32x4_t{(uint32_t)lst[nb][e], (uint32_t)(lst[nb][e] >> 32),
+                        (uint32_t)lst[nb][e + 1], (uint32_t)(lst[nb][e + 1] >> 32)};
+        }
+      }
+    }
+  }
+}
+
 // binary32 value of a canonical key (NaN keys give a quiet NaN)
 struct KeyValue {
   __device__ float operator()(int, uint32_t, uint32_t key) const {
@@ -262,8 +465,6 @@ struct KeyValue {
     return __uint_as_float((key & 0x80000000u) ? (key ^ 0x80000000u) : ~key);
   }
 };
-
-int lm_passes(int M) { return (M + kLmCols - 1) / kLmCols; }
 
 // Waves that share the vocabulary blocks evenly: the fewest waves (at most kLmMaxWaves)
 // for the smallest number of blocks per wave, so no wave has a block more than another.
@@ -300,11 +501,22 @@ extern "C" int dflash2_lmhead_topk16(const void* hidden, int64_t hid_seq_stride,
     return DFLASH2_EWORKSPACE;
   const int M = B * N;
   uint64_t* lists = (uint64_t*)ws;
-  const int nwaves = lm_waves(V);
-  const int nlists = (nwaves + kLmWaves - 1) / kLmWaves;  // one per workgroup
-  lmhead_stream_kernel<<<dim3(nlists, lm_passes(M)), 64 * kLmWaves, 0, stream>>>(
-      (const uint16_t*)hidden, hid_seq_stride, hid_row_stride, row0, N, M,
-      (const uint16_t*)weight, C, V, nwaves, lists);
+  int nlists;  // one per workgroup
+  if (M <= kLmCols) {
+    const int nwaves = lm_waves(V);
+    nlists = (nwaves + kLmWaves - 1) / kLmWaves;
+    lmhead_stream_kernel<<<dim3(nlists, 1), 64 * kLmWaves, 0, stream>>>(
+        (const uint16_t*)hidden, hid_seq_stride, hid_row_stride, row0, N, M,
+        (const uint16_t*)weight, C, V, nwaves, lists);
+  } else {
+    // groups of four vocabulary blocks shared evenly by at most kLmMaxWGs workgroups
+    const int ngroups = ((V + kLmRows - 1) / kLmRows + kLmWaves - 1) / kLmWaves;
+    const int per = (ngroups + kLmMaxWGs - 1) / kLmMaxWGs;
+    nlists = (ngroups + per - 1) / per;
+    lmhead_tiled_kernel<<<dim3(nlists, (M + kTlCols - 1) / kTlCols), 64 * kLmWaves, 0, stream>>>(
+        (const uint16_t*)hidden, hid_seq_stride, hid_row_stride, row0, N, M,
+        (const uint16_t*)weight, C, V, ngroups, lists);
+  }
   merge16_kernel<KeyValue><<<M, kMergeThreads, (size_t)nlists * sizeof(uint64_t), stream>>>(
       nlists, lists, idx, val, KeyValue{});
   return launch_status();

@@ -76,10 +76,12 @@ def _rand(rng, shape, scale):
 
 
 @pytest.mark.parametrize("B,N,C,V", [(1, 7, 256, 1000), (2, 3, 128, 32), (1, 1, 384, 16),
-                                     (5, 7, 512, 3001)])
+                                     (5, 7, 512, 3001), (16, 7, 512, 3001), (19, 7, 256, 4097),
+                                     (12, 4, 128, 16), (64, 7, 128, 700)])
 def test_lmhead_small_shapes(d2, B, N, C, V):
-    # ragged last vocabulary block, a single block, V = 16, and more than 32 hidden rows
-    # (two passes over the weight)
+    # up to 32 hidden rows: ragged last vocabulary block, a single block, V = 16; more
+    # than 32 (the tiled kernel, 128 rows per pass): a ragged row tile, two and four passes,
+    # a vocabulary smaller than one workgroup's four blocks
     rng = np.random.default_rng(B * 1000 + N * 100 + C + V)
     hid = _rand(rng, (B, N + 1, C), 2.0)
     w = _rand(rng, (V, C), 1.0 / np.sqrt(C))
@@ -93,6 +95,16 @@ def test_lmhead_integer_data_is_exact_with_ties(d2):
     w = rng.integers(-1, 2, size=(V, C)).astype(np.float32)
     w[[100, 4000, 8999]] = w[5]                            # exact ties across blocks and waves
     run_case(d2, hid, B, N, 0, N * C, C, wl.to_bf16_bits(w), "integer data", exact=True)
+
+
+def test_lmhead_integer_data_many_rows_exact(d2):
+    # the tiled kernel on exact data: 42 hidden rows, ties across workgroups
+    rng = np.random.default_rng(93)
+    B, N, C, V = 6, 7, 640, 9000
+    hid = wl.to_bf16_bits(rng.integers(-2, 3, size=(B, N, C)).astype(np.float32))
+    w = rng.integers(-1, 2, size=(V, C)).astype(np.float32)
+    w[[31, 32, 4000, 8999]] = w[7]
+    run_case(d2, hid, B, N, 0, N * C, C, wl.to_bf16_bits(w), "integer data, 42 rows", exact=True)
 
 
 def test_lmhead_strides_and_broadcast(d2):
@@ -115,3 +127,20 @@ def test_lmhead_drafter_geometry(d2):
     gi, oi = run_case(d2, hid, 1, cfg.N, 1, cfg.P * cfg.C, cfg.C, w, "drafter geometry")
     # with continuous data the order is essentially unambiguous
     assert (gi == oi).mean() > 0.95
+
+
+def test_lmhead_drafter_geometry_batch16_sampled(d2):
+    # 16 sequences x 7 proposal rows (one 128-row tile) on the drafter's head; the oracle
+    # is evaluated on a sample of the 112 rows
+    cfg = wl.CONFIGS[2]
+    B, N, P, C = 16, cfg.N, cfg.P, cfg.C
+    w = wl.head_weight(cfg)
+    rng = np.random.default_rng(94)
+    hid = _rand(rng, (B, P, C), float(np.sqrt(cfg.draft_var)))
+    say(f"lmhead_topk16 drafter geometry B={B} N={N} C={C} V={w.shape[0]}")
+    gi, gv = run_gpu(d2, hid, B, N, 1, P * C, C, w)
+    sample = [0, 6, 31, 32, 63, 64, 95, 111]
+    rows = np.stack([hid[m // N, 1 + m % N] for m in sample])
+    oi, L, A = orc.lmhead_topk16(rows, 1, len(sample), 0, 0, C, w)
+    check_valid(gi[sample], gv[sample], L, A, C, "drafter geometry B16 sample")
+    assert (gi[sample] == oi.reshape(len(sample), 16)).mean() > 0.95
