@@ -77,6 +77,20 @@ __device__ __forceinline__ void merge_top16(uint64_t (&a)[kTopK], const uint64_t
       if ((i & d) == 0) cx_desc(a[i], a[i + d]);
 }
 
+// a sorted descending by a bitonic sorting network (80 compare-exchanges, no branches)
+__device__ __forceinline__ void sort16_desc(uint64_t (&a)[kTopK]) {
+#pragma unroll
+  for (int k = 2; k <= kTopK; k <<= 1)
+#pragma unroll
+    for (int d = k >> 1; d >= 1; d >>= 1)
+#pragma unroll
+      for (int i = 0; i < kTopK; ++i)
+        if ((i & d) == 0) {
+          if ((i & k) == 0) cx_desc(a[i], a[i + d]);
+          else cx_desc(a[i + d], a[i]);
+        }
+}
+
 // Eight 16-byte loads at p + 16 k elements, k = 0..7, in inline assembly: the compiler
 // would otherwise wait for every load in flight before the first use. The caller's explicit
 // vmcnt waits cover them (loads retire in order), and tie8 then marks the registers as
@@ -259,12 +273,14 @@ __global__ __launch_bounds__(64 * kLmWaves) void lmhead_stream_kernel(
 // 64-column chunks of four neighbouring vocabulary blocks (one per wave, 32 rows each),
 // and share a tile of 128 hidden rows x 64 columns that the four waves copy into LDS
 // together (a quarter each). Per chunk a wave does 4 k-steps x 4 column blocks = 16
-// MFMA into four accumulators. Head and hidden tiles go through rings of four LDS
-// buffers, three chunks in flight: chunk i + 3 is issued after the barrier that follows
-// chunk i's wait, into the buffers chunk i - 1 used (every wave has finished it by then).
-// 16-byte chunks of the 128-byte LDS rows are XOR-swizzled by (row / 2) % 8, so both
-// operands' reads hit distinct banks. Each lane keeps four sorted lists (one per column
-// block); at the end the workgroup merges them as in the small kernel.
+// MFMA into four accumulators. Head tiles (from HBM) and hidden tiles (from L2) go
+// through rings of four LDS buffers, three chunks in flight: after the barrier that
+// follows chunk i's wait, chunk i + 3 is issued into the buffers chunk i - 1 used (every
+// wave has finished it by then). Loads retire in order, so one wait count serves both
+// rings; a deeper head ring would not help, since waiting for a hidden tile also waits
+// for every head tile issued before it. 16-byte chunks of the 128-byte LDS rows are XOR-swizzled by (row / 2) % 8, so
+// both operands' reads hit distinct banks. Each lane keeps four sorted lists (one per
+// column block); at the end the workgroup merges them as in the small kernel.
 constexpr int kTlCols = 128;                   // hidden rows per pass
 constexpr int kTlChunk = 64;                   // columns per chunk
 constexpr int kTlBufs = 4;
@@ -277,11 +293,25 @@ __device__ __forceinline__ int tl_swz(int r) { return (r >> 1) & 7; }
 struct TiledSmem {
   union {
     struct {
-      uint16_t w[kLmWaves][kTlBufs][kTlW];
-      uint16_t h[kTlBufs][kTlH];
+      uint16_t w[kLmWaves][kTlBufs][kTlW];     // 64 KiB
+      uint16_t h[kTlBufs][kTlH];               // 64 KiB
     } ring;
     uint64_t lists[kLmWaves][kTlCols][kTopK];  // 64 KiB, for the final merge
   };
+};
+
+// position in a workgroup's sequence of (block group, column chunk) items; it stops at
+// the last item, so copies issued past the end repeat the last one (never used)
+struct TlCursor {
+  int g = 0, k = 0, n = 0;
+  __device__ __forceinline__ void next(int nch, int items) {  // selects, no branches
+    const int step = n + 1 < items ? 1 : 0;
+    n += step;
+    k += step;
+    const int wrap = k == nch ? 1 : 0;
+    k = wrap ? 0 : k;
+    g += wrap;
+  }
 };
 
 __global__ __launch_bounds__(64 * kLmWaves) void lmhead_tiled_kernel(
@@ -291,43 +321,46 @@ __global__ __launch_bounds__(64 * kLmWaves) void lmhead_tiled_kernel(
   const int t = threadIdx.x, lane = t & 63, n = lane & 31, hh = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int nwg = gridDim.x;
-  const int nblocks = (V + kLmRows - 1) / kLmRows;
   const int nch = C / kTlChunk;
   // block group g (four neighbouring blocks) of workgroup x is x + g * nwg
   const int mygroups = blockIdx.x < ngroups ? (ngroups - 1 - blockIdx.x) / nwg + 1 : 0;
   const int items = mygroups * nch;
   const int mbase = blockIdx.y * kTlCols;
 
-  // this wave's share of the hidden tile: rows 32w + 8q + lane/8, q < 4 (clamped to M - 1)
+  // copy lanes: 8 per 128-byte row, rows 8q + lane/8 of a 32-row quarter, q < 4
   const int lrow = lane >> 3;
-  const uint16_t* hsrc[4];
+  const uint16_t* hsrc[4];  // this wave's quarter of the hidden tile (rows clamped to M - 1)
+  int wsw[4];               // swizzled column of the head copy lanes, in elements
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int r = 32 * w + 8 * q + lrow;
-    int mr = mbase + r;
+    const int r = 8 * q + lrow;
+    int mr = mbase + 32 * w + r;
     mr = mr < M ? mr : M - 1;
     hsrc[q] = hid + (int64_t)(mr / N) * hss + (int64_t)(row0 + mr % N) * hrs +
-              8 * ((lane & 7) ^ tl_swz(r));
+              8 * ((lane & 7) ^ tl_swz(32 * w + r));
+    wsw[q] = 8 * ((lane & 7) ^ tl_swz(r));
   }
-  auto issue = [&](int item, int slot) {
-    item = item < items ? item : items - 1;  // past the end: a copy of the last one, unused
-    const int g = item / nch, k = item - g * nch;
-    const int blk = 4 * (blockIdx.x + g * nwg) + w;
-    const int v0 = blk * kLmRows;
-    const int c0 = k * kTlChunk;
+  auto issue_w = [&](const TlCursor& c, int slot) {
+    // rows at or past the end read row V - 1 (their products are never used)
+    int v0 = (4 * (blockIdx.x + c.g * nwg) + w) * kLmRows;
+    v0 = v0 < V ? v0 : V - 1;
+    const int lim = V - 1 - v0;
+    const uint16_t* base = wt + (int64_t)v0 * C + c.k * kTlChunk;
     uint16_t* dw = &sm.ring.w[w][slot][0];
-    uint16_t* dh = &sm.ring.h[slot][(32 * w) * kTlChunk];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int r = 8 * q + lrow;
-      const int v = v0 + r < V ? v0 + r : V - 1;
-      const uint16_t* src = wt + (int64_t)v * C + c0 + 8 * ((lane & 7) ^ tl_swz(r));
-      __builtin_amdgcn_global_load_lds((const void*)src, DF2_LDS(dw + q * 512), 16, 0, 0);
+      const int off = (r < lim ? r : lim) * C + wsw[q];
+      __builtin_amdgcn_global_load_lds((const void*)(base + off), DF2_LDS(dw + q * 512), 16,
+                                       0, 0);
     }
+  };
+  auto issue_h = [&](const TlCursor& c, int slot) {
+    uint16_t* dh = &sm.ring.h[slot][(32 * w) * kTlChunk];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      __builtin_amdgcn_global_load_lds((const void*)(hsrc[q] + c0), DF2_LDS(dh + q * 512), 16,
-                                       0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(hsrc[q] + c.k * kTlChunk),
+                                       DF2_LDS(dh + q * 512), 16, 0, 0);
   };
 
   uint64_t lst[kTlNB][kTopK];
@@ -344,19 +377,32 @@ __global__ __launch_bounds__(64 * kLmWaves) void lmhead_tiled_kernel(
     const int g = item / nch, k = item - g * nch;
     const uint16_t* tw = &sm.ring.w[w][slot][0];
     const uint16_t* th = &sm.ring.h[slot][0];
+    // one wave per SIMD: LDS latency is hidden only by reads in flight, so the operand
+    // reads run ahead of the products (the schedule is fixed below)
+    u32x4_t a[kTlChunk / 16], bop[kTlChunk / 16][kTlNB];
 #pragma unroll
     for (int ks = 0; ks < kTlChunk / 16; ++ks) {
       const int ch = 8 * ((2 * ks + hh) ^ swn);
-      const u32x4_t a = *reinterpret_cast<const u32x4_t*>(tw + n * kTlChunk + ch);
+      a[ks] = *reinterpret_cast<const u32x4_t*>(tw + n * kTlChunk + ch);
 #pragma unroll
-      for (int nb = 0; nb < kTlNB; ++nb) {
-        const u32x4_t bop =
+      for (int nb = 0; nb < kTlNB; ++nb)
+        bop[ks][nb] =
             *reinterpret_cast<const u32x4_t*>(th + (nb * kLmCols + n) * kTlChunk + ch);
-        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                          __builtin_bit_cast(bf16x8_t, bop),
-                                                          acc[nb], 0, 0, 0);
-      }
     }
+#pragma unroll
+    for (int ks = 0; ks < kTlChunk / 16; ++ks)
+#pragma unroll
+      for (int nb = 0; nb < kTlNB; ++nb)
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[ks]),
+                                                          __builtin_bit_cast(bf16x8_t, bop[ks][nb]),
+                                                          acc[nb], 0, 0, 0);
+    // reads of two k-steps ahead, then each k-step's products behind the next one's reads
+    __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     if (k == nch - 1) {
       const int v0 = (4 * (blockIdx.x + g * nwg) + w) * kLmRows;
 #pragma unroll
@@ -372,18 +418,8 @@ __global__ __launch_bounds__(64 * kLmWaves) void lmhead_tiled_kernel(
           cmax = cand[i] > cmax ? cand[i] : cmax;
         }
         if (__ballot(cmax > lst[nb][kTopK - 1])) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            uint64_t c = cand[i];
-            if (__ballot(c > lst[nb][kTopK - 1])) {
-#pragma unroll
-              for (int e = 0; e < kTopK; ++e) {
-                const uint64_t hi = lst[nb][e] > c ? lst[nb][e] : c;
-                c = lst[nb][e] > c ? c : lst[nb][e];
-                lst[nb][e] = hi;
-              }
-            }
-          }
+          sort16_desc(cand);
+          merge_top16(lst[nb], cand);
         }
         acc[nb] = f32x16_t{};
       }
@@ -391,14 +427,21 @@ __global__ __launch_bounds__(64 * kLmWaves) void lmhead_tiled_kernel(
   };
 
   if (items > 0) {
-    issue(0, 0);
-    issue(1, 1);
-    issue(2, 2);
+    TlCursor ci;  // next chunk to issue
+#pragma unroll
+    for (int j = 0; j < kTlBufs - 1; ++j) {
+      issue_w(ci, j);
+      issue_h(ci, j);
+      ci.next(nch, items);
+    }
     for (int i = 0; i < items; ++i) {
       asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // chunk i's 8 copies have landed
       __builtin_amdgcn_s_barrier();                         // ... everyone's, and i - 1 is done
-      issue(i + 3, (i + 3) & (kTlBufs - 1));
-      compute(i, i & (kTlBufs - 1));
+      const int slot = i & (kTlBufs - 1);
+      issue_w(ci, (slot + kTlBufs - 1) & (kTlBufs - 1));
+      issue_h(ci, (slot + kTlBufs - 1) & (kTlBufs - 1));
+      ci.next(nch, items);
+      compute(i, slot);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
