@@ -6,9 +6,10 @@ single-threaded reference that the GPU library is checked against. Only the test
 product path (``block_drafter_draft_amd``) never does, and shares no code with it.
 
 Each wrapper marshals numpy arrays into the C functions; the arithmetic and the citations
-of the pages live in the C file. The one exception is the output-head projection (the
-``lmhead_*`` functions at the end), written here with numpy: a binary64 matrix product of
-the exact bf16 values, and the top-16 order applied to its rows. Functions that are pinned
+of the pages live in the C file. The exceptions are the output-head projection (the
+``lmhead_*`` functions) and the drafter projections (``proj``, ``conv_coeffs``,
+``selector_gate``), written here with numpy: a binary64 matrix product of the exact bf16
+values (and, for the head, the top-16 order applied to its rows). Functions that are pinned
 by tests are listed in ``tests/test_oracle_pins.py``.
 """
 from __future__ import annotations
@@ -326,6 +327,60 @@ def lmhead_topk16(hidden, B, N, row0, seq_stride, row_stride, weight):
     idx = np.stack([top16_order_f64(L[m]) for m in range(B * N)]).reshape(B, N, K)
     return idx, L, A
 
+
+
+# ------------------------------------------------------------------------------------------
+# The drafter's projections on either side of the path ("[Spec Decode] DFlash2: local
+# convolution + candidate selector - #52816", PR description: the dynamic conv wraps each
+# sublayer in and out, its per-group coefficients coming from one projection of the
+# sublayer's input; the selector's edge multiplies A[p] elementwise by a projection of the
+# hidden state, project(h). "qwen35: DSpark speculative decoding (Qwen3.8-27B drafters) -
+# #625", DFlash 2 commit: the conv's kernel projections and the selector's hproj).
+# Readings: both are plain linear maps, no bias and no nonlinearity; a coefficient row of
+# a sublayer is ordered (conv s, tap t, group g) -> (2 s + t) G + g, s = 0 the conv before
+# the sublayer and s = 1 the one after; the selector gate of slot i is the projection of
+# slot i's hidden row.
+# ------------------------------------------------------------------------------------------
+
+
+def gather_rows(hidden, B, N, row0, seq_stride, row_stride, C) -> np.ndarray:
+    """Rows row0..row0+N-1 of each of the B sequences of a flat buffer addressed by element
+    strides, as an array [B*N, C] (sequence-major)."""
+    h = np.ascontiguousarray(hidden).reshape(-1)
+    return np.stack([h[b * seq_stride + (row0 + r) * row_stride:
+                       b * seq_stride + (row0 + r) * row_stride + C]
+                     for b in range(B) for r in range(N)])
+
+
+def proj(hidden, B, N, row0, seq_stride, row_stride, weight):
+    """y[b, r, o] = sum_c hidden[b*seq_stride + (row0 + r)*row_stride + c] * weight[o, c] for
+    bf16-bit hidden rows and a bf16-bit weight [O, C] (a linear layer's usual layout), in
+    binary64 (the exact products summed; within C * 2^-53 * abs_sum of the exact sum).
+    Returns (Y [B, N, O], A [B, N, O]) with A the sums of |h w|."""
+    O, C = weight.shape
+    rows = gather_rows(hidden, B, N, row0, seq_stride, row_stride, C)
+    Y, A = lmhead_logits(rows, weight)
+    return Y.reshape(B, N, O), A.reshape(B, N, O)
+
+
+def conv_coeffs(x_in, w_delta, G):
+    """The dynamic coefficients of the two convs around one sublayer, from one projection of
+    the sublayer's input x_in [B, P, C] (bf16 bits) with w_delta [4 G, C] (bf16 bits):
+    returns (delta_in, delta_out), each [B, P, 2, G] binary32 (the binary64 sums rounded
+    once), in the layout the conv takes (tap-major within a position)."""
+    B, P, C = x_in.shape
+    Y, _ = proj(x_in.reshape(-1), B, P, 0, P * C, C, w_delta)
+    d = Y.astype(np.float32).reshape(B, P, 2, 2, G)
+    return np.ascontiguousarray(d[:, :, 0]), np.ascontiguousarray(d[:, :, 1])
+
+
+def selector_gate(hidden, w_gate, N=None):
+    """g[b, i-1] = project(h[b, i]) for block slots i = 1..N (slot 0, the anchor, is not
+    scored), hidden [B, P, C] and w_gate [R, C] bf16 bits; binary32 [B, N, R]."""
+    B, P, C = hidden.shape
+    N = P - 1 if N is None else N
+    Y, _ = proj(hidden.reshape(-1), B, N, 1, P * C, C, w_gate)
+    return Y.astype(np.float32)
 
 # ------------------------------------------------------------------------------------------
 # Context-ring maintenance after verification ("Geramy/LSE docs/DFLASH2.md", native-test

@@ -944,3 +944,82 @@ def test_ddtree_is_the_top_budget_nodes(orc, budget):
             assert abs(sc[b, t] - want[t][0]) < 1e-4
             taken[path] = t
     assert not st.any()
+
+
+# ----------------------------------------------------------------------------------------
+# Drafter projections: conv coefficients and the selector gate
+# ----------------------------------------------------------------------------------------
+
+def test_proj_addressing_with_one_hot_weights(orc):
+    # every element of the (padded, strided) hidden buffer holds a distinct small integer
+    # (exact in bf16); weight row o is s_o * e_{c(o)}, so y[b, r, o] must be exactly
+    # s_o * buf[b*ss + (row0 + r)*rs + c(o)], each index computed here by hand
+    rng = np.random.default_rng(91)
+    B, N, row0, C, O = 3, 4, 2, 40, 29
+    rs, ss = C + 8, (N + row0 + 1) * (C + 8) + 16
+    buf = ((np.arange(B * ss) * 7) % 251 - 125).astype(np.float32)
+    col = rng.integers(0, C, size=O)
+    sc = rng.choice([1.0, -2.0, 0.5], size=O).astype(np.float32)
+    w = np.zeros((O, C), np.float32)
+    w[np.arange(O), col] = sc
+    Y, A = orc.proj(to_bf16_bits(buf), B, N, row0, ss, rs, to_bf16_bits(w))
+    assert Y.shape == (B, N, O)
+    for b in range(B):
+        for r in range(N):
+            for o in range(O):
+                want = float(sc[o]) * float(buf[b * ss + (row0 + r) * rs + int(col[o])])
+                assert Y[b, r, o] == want and A[b, r, o] == abs(want)
+
+
+def test_proj_matches_fsum_and_torch_linear(orc):
+    # against a correctly rounded sum of the exact products (math.fsum), element by element,
+    # and against torch's linear layer in binary64 (y = x W^T) on a non-square weight
+    import math
+    rng = np.random.default_rng(92)
+    B, N, C, O = 2, 3, 72, 11
+    h = to_bf16_bits(rng.standard_normal((B, N, C)).astype(np.float32) * 2)
+    w = to_bf16_bits(rng.standard_normal((O, C)).astype(np.float32) / 4)
+    Y, A = orc.proj(h.reshape(-1), B, N, 0, N * C, C, w)
+    hf, wf = bf16_bits_to_f32(h).astype(float), bf16_bits_to_f32(w).astype(float)
+    for b in range(B):
+        for r in range(N):
+            for o in range(O):
+                prods = [hf[b, r, c] * wf[o, c] for c in range(C)]
+                assert abs(Y[b, r, o] - math.fsum(prods)) <= C * 2.0**-53 * A[b, r, o]
+    ref = torch.nn.functional.linear(torch.from_numpy(hf), torch.from_numpy(wf)).numpy()
+    np.testing.assert_allclose(Y, ref, rtol=0, atol=1e-12)
+
+
+def test_conv_coeffs_layout(orc):
+    # one projection of the sublayer input gives both convs' coefficients: weight row
+    # (2 s + t) G + g is a one-hot on column c(s, t, g), so delta_s[b, i, t, g] must be
+    # x[b, i, c(s, t, g)] exactly (s = 0: the conv before the sublayer, s = 1: after)
+    rng = np.random.default_rng(93)
+    B, P, C, G = 2, 8, 64, 4
+    x = ((np.arange(B * P * C).reshape(B, P, C) * 5) % 199 - 99).astype(np.float32)
+    col = rng.integers(0, C, size=(2, 2, G))
+    w = np.zeros((4 * G, C), np.float32)
+    for s, t, g in itertools.product(range(2), range(2), range(G)):
+        w[(2 * s + t) * G + g, col[s, t, g]] = 1.0
+    d_in, d_out = orc.conv_coeffs(to_bf16_bits(x), to_bf16_bits(w), G)
+    assert d_in.shape == (B, P, 2, G) and d_in.dtype == np.float32
+    for s, d in enumerate((d_in, d_out)):
+        for b, i, t, g in itertools.product(range(B), range(P), range(2), range(G)):
+            assert d[b, i, t, g] == x[b, i, col[s, t, g]]
+
+
+def test_selector_gate_takes_slots_one_to_n(orc):
+    # the gate of slot i comes from slot i's hidden row: rows are made distinct by a
+    # constant per (b, slot) in column 0 and the weight reads only column 0
+    B, P, C, R = 2, 8, 32, 16
+    h = np.zeros((B, P, C), np.float32)
+    for b in range(B):
+        for i in range(P):
+            h[b, i, 0] = 10 * b + i
+    w = np.zeros((R, C), np.float32)
+    w[:, 0] = np.arange(1, R + 1)
+    g = orc.selector_gate(to_bf16_bits(h), to_bf16_bits(w))
+    assert g.shape == (B, P - 1, R) and g.dtype == np.float32
+    for b in range(B):
+        for i in range(1, P):
+            np.testing.assert_array_equal(g[b, i - 1], (10 * b + i) * np.arange(1, R + 1))
