@@ -123,7 +123,7 @@ def main():
                     help="input sets to rotate (default: enough to exceed the last-level cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-lmhead", action="store_true",
-                    help="skip the separate output-head projection + top-16 measurement")
+                    help="skip the separate output-head + top-16 and projection measurements")
     ap.add_argument("--no-q8", action="store_true",
                     help="skip the separate Q8-selector and draft-tree measurements")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -286,6 +286,57 @@ def main():
                   "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": lm_gbs / HBM_PEAK_GBS}
         del head
 
+    # The drafter projections beside the step (calls outside it): per conv site, the
+    # coefficients from one projection of the sublayer's input (2G of the sublayer's 4G
+    # weight rows), and once per step the selector gate from block rows 1..N. Weights are
+    # N(0, 1/C) bf16, drawn on the device; three copies of every weight rotate so that the
+    # replays read them from HBM rather than the last-level cache. Algorithmic bytes: one
+    # read of the weight rows and the hidden rows, one write of the outputs.
+    proj = None
+    if not args.no_lmhead and cfg.act_bf16:
+        G, C = cfg.C // 16, cfg.C
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(0xDF2F + cfg.cfg)
+        ncopy = 3
+        subs = cfg.layers * 2
+
+        def rand_w(rows):
+            return (torch.randn((rows, C), generator=gen, device=dev) * (1.0 / math.sqrt(C))).to(torch.bfloat16)
+        wconv = [[rand_w(4 * G) for _ in range(subs)] for _ in range(ncopy)]
+        wgate = [rand_w(cfg.R) for _ in range(ncopy)]
+        dbuf = torch.empty((cfg.sites, B, P, 2 * G), dtype=torch.float32, device=dev)
+        gbuf = torch.empty((B, N, cfg.R), dtype=torch.float32, device=dev)
+        ghid = torch.from_numpy(wl.head_hidden(cfg).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        def coeff_call(r):
+            x = inputs[r % nsets]
+            site = r % cfg.sites
+            sub, half = site // 2, site % 2
+            w = wconv[(r // cfg.sites) % ncopy][sub][half * 2 * G:(half + 1) * 2 * G]
+            d2.proj(x.conv_x[site - half], B, P, 0, P * C, C, w, out=dbuf[site])
+
+        def gate_call(r):
+            d2.proj(ghid, B, N, 1, P * C, C, wgate[r % ncopy], out=gbuf)
+
+        coeff_call(0)
+        gate_call(0)
+        torch.cuda.synchronize()
+        c_ms = timed(coeff_call, ncopy * cfg.sites)
+        g_ms = timed(gate_call, ncopy * 4)
+        c_bytes = float(2 * G * C * 2 + B * P * C * 2 + B * P * 2 * G * 4)
+        g_bytes = float(cfg.R * C * 2 + B * N * C * 2 + B * N * cfg.R * 4)
+        proj = {"call": "dflash2_proj",
+                "conv_coeffs": {"rows": B * P, "outputs": 2 * G, "width": C,
+                                "calls_per_step": cfg.sites, "us_per_call": c_ms * 1e3,
+                                "bytes_per_call": c_bytes,
+                                "achieved": c_bytes / (c_ms * 1e-3) / 1e9},
+                "selector_gate": {"rows": B * N, "outputs": cfg.R, "width": C,
+                                  "calls_per_step": 1, "us_per_call": g_ms * 1e3,
+                                  "bytes_per_call": g_bytes,
+                                  "achieved": g_bytes / (g_ms * 1e-3) / 1e9},
+                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+        del wconv, wgate
+
     # The selector over affine-Q8 codebooks (a call outside the step): the workload's bf16
     # codebooks converted to Q8 (groups of 64), same candidates, gates and anchors.
     select_q8 = None
@@ -364,6 +415,7 @@ def main():
         "mean_accepted": mean_acc,
         "cpu_baseline": None,
         "lmhead_topk16": lmhead,
+        "proj": proj,
         "select_q8": select_q8,
         "ddtree": ddtree,
     }

@@ -124,6 +124,7 @@ _T_CTX, _T_Q, _T_KBLK, _T_VBLK, _T_KRING, _T_VRING = 1, 2, 3, 4, 5, 6
 _T_X, _T_BASE, _T_DELTA = 7, 8, 9
 _T_DRAFT, _T_TNOISE, _T_PRED, _T_SUCC, _T_GATE, _T_ANCHOR = 10, 11, 12, 13, 14, 15
 _T_HIDDEN, _T_HEAD = 16, 17
+_T_CONVPROJ, _T_GATEPROJ = 18, 19
 
 
 def _rng(cfg: Config, tensor: int, *more: int) -> np.random.Generator:
@@ -272,6 +273,19 @@ def head_weight(cfg: Config, V: int | None = None, chunk: int = 16384) -> np.nda
         v1 = min(V, v0 + chunk)
         out[v0:v1] = to_bf16_bits(_normal(_rng(cfg, _T_HEAD, c), (v1 - v0, cfg.C), 1.0 / cfg.C))
     return out
+
+
+def conv_proj_weight(cfg: Config, layer: int, sub: int) -> np.ndarray:
+    """Coefficient projection of one sublayer (sub 0: attention, 1: MLP) of a layer,
+    [4 G, C] bf16 bits ~ N(0, 1/C): rows (conv s, tap t, group g) -> (2 s + t) G + g, s = 0
+    the conv before the sublayer and s = 1 the one after."""
+    G = cfg.C // 16
+    return to_bf16_bits(_normal(_rng(cfg, _T_CONVPROJ, layer, sub), (4 * G, cfg.C), 1.0 / cfg.C))
+
+
+def gate_proj_weight(cfg: Config) -> np.ndarray:
+    """Selector gate projection [R, C] bf16 bits ~ N(0, 1/C)."""
+    return to_bf16_bits(_normal(_rng(cfg, _T_GATEPROJ), (cfg.R, cfg.C), 1.0 / cfg.C))
 
 
 def anchor(cfg: Config, iset: int = 0) -> np.ndarray:

@@ -162,6 +162,35 @@ int dflash2_lmhead_topk16(const void *hidden, int64_t hid_seq_stride, int64_t hi
 size_t dflash2_lmhead_topk16_workspace_bytes(int B, int N, int V, int C);
 
 /*
+ * dflash2_proj - the drafter's linear projections on either side of the path: the dynamic
+ * conv's per-group coefficients, taken from one projection of the sublayer's input, and
+ * the selector gate, a projection of each block slot's hidden state that multiplies the
+ * predecessor codebook row elementwise ("[Spec Decode] DFlash2: local convolution +
+ * candidate selector - #52816", PR description, both items; "qwen35: DSpark speculative
+ * decoding (Qwen3.8-27B drafters) - #625", DFlash 2 commit: kernel projections, hproj).
+ *
+ *   out[b*out_seq_stride + r*out_row_stride + o]
+ *       = sum_c hidden[b*hid_seq_stride + (row0 + r)*hid_row_stride + c] * weight[o*C + c]
+ *
+ *   hidden  bf16, rows r < N of each of the B sequences, C elements each (strides may be 0)
+ *   weight  bf16 [O, C] row-major (a linear layer's usual layout)
+ *   out     f32; the B*N output rows of O values must not overlap (sequence-major or
+ *           row-major placement, else DFLASH2_EINVAL); out may not alias the inputs
+ * The bf16 products are exact; they are summed in binary32 in a fixed order (the result
+ * does not vary between calls), within C * 2^-24 * sum_c |h_c w_c| of the exact sum for
+ * ordinary magnitudes. Conv coefficients: with a sublayer's coefficient weight [4G, C]
+ * ordered (conv s, tap t, group g) -> (2s + t)G + g, the first 2G rows give the conv
+ * before the sublayer and the last 2G the conv after it, each [B, P, 2, G] as
+ * dflash2_dynconv2 takes delta (one call per half, weight offset by 2G*C). Selector gate:
+ * weight [R, C], rows row0 = 1 .. N of the block, out [B, N, R]. Requires C % 8 == 0,
+ * 16-byte aligned hidden and weight, hidden strides multiples of 8, B*N <= 2^20,
+ * O <= 2^26. No workspace.
+ */
+int dflash2_proj(const void *hidden, int64_t hid_seq_stride, int64_t hid_row_stride, int row0,
+                 const void *weight, int C, int O, int B, int N, float *out,
+                 int64_t out_seq_stride, int64_t out_row_stride, hipStream_t stream);
+
+/*
  * dflash2_ring_update - keeps a drafter context ring in step with the committed sequence
  * after verification ("Geramy/LSE docs/DFLASH2.md", native-test notes: cache rewind,
  * replacement and reset). Position p of sequence b lives in ring slot p mod S (the layout

@@ -240,3 +240,23 @@ def test_ring_update_rejects():
     assert call(dt=9) == d2.EUNSUPPORTED
     assert call(Hkv=1, D=3) == d2.EUNSUPPORTED         # rows not whole 16-byte pieces
     assert call(kr=ctypes.c_void_p(0x100008)) == d2.EUNSUPPORTED
+
+
+def test_proj_rejects():
+    L = d2.lib()
+
+    def call(hid=FAKE, w=FAKE, C=5120, O=640, B=2, N=8, row0=0, ss=8 * 5120, rs=5120,
+             out=FAKE, oss=8 * 640, ors=640):
+        return L.dflash2_proj(hid, ss, rs, row0, w, C, O, B, N, out, oss, ors, None)
+    assert call(hid=NUL) == d2.EINVAL
+    assert call(out=NUL) == d2.EINVAL
+    assert call(B=0) == d2.EINVAL
+    assert call(O=0) == d2.EINVAL
+    assert call(row0=-1) == d2.EINVAL
+    assert call(ss=-8) == d2.EINVAL
+    assert call(ors=600) == d2.EINVAL                  # output rows would overlap
+    assert call(oss=640) == d2.EINVAL                  # sequences would overlap
+    assert call(C=5124) == d2.EUNSUPPORTED             # not a multiple of 8
+    assert call(rs=5121) == d2.EUNSUPPORTED            # row stride not a multiple of 8
+    assert call(w=ctypes.c_void_p(0x100008)) == d2.EUNSUPPORTED
+    assert call(B=1 << 18, N=8) == d2.EUNSUPPORTED     # more than 2^20 rows
