@@ -307,16 +307,18 @@ def main():
         dbuf = torch.empty((cfg.sites, B, P, 2 * G), dtype=torch.float32, device=dev)
         gbuf = torch.empty((B, N, cfg.R), dtype=torch.float32, device=dev)
         ghid = torch.from_numpy(wl.head_hidden(cfg).view(np.int16)).view(torch.bfloat16).to(dev)
+        c_ws = d2.workspace(d2.proj_workspace_bytes(B, P, 2 * G, C), dev)
+        g_ws = d2.workspace(d2.proj_workspace_bytes(B, N, cfg.R, C), dev)
 
         def coeff_call(r):
             x = inputs[r % nsets]
             site = r % cfg.sites
             sub, half = site // 2, site % 2
             w = wconv[(r // cfg.sites) % ncopy][sub][half * 2 * G:(half + 1) * 2 * G]
-            d2.proj(x.conv_x[site - half], B, P, 0, P * C, C, w, out=dbuf[site])
+            d2.proj(x.conv_x[site - half], B, P, 0, P * C, C, w, out=dbuf[site], ws=c_ws)
 
         def gate_call(r):
-            d2.proj(ghid, B, N, 1, P * C, C, wgate[r % ncopy], out=gbuf)
+            d2.proj(ghid, B, N, 1, P * C, C, wgate[r % ncopy], out=gbuf, ws=g_ws)
 
         coeff_call(0)
         gate_call(0)

@@ -20,8 +20,14 @@
 // m0 + r: the four lanes of a row read 64 contiguous bytes, and the pair of steps s, s + 1
 // completes a 128-byte line. All NS steps' loads of a pass are issued before the first
 // product. The waves' 16 x 16 partial tiles are then added in wave order through LDS, so
-// the result does not depend on timing. At batch 1 the call is a latency-bound read of
-// the weight (6.5 MB for a conv site's 640 coefficients at width 5120).
+// the result does not depend on timing.
+//
+// A compute unit keeps only so many lines in flight, so a small call is paced by how many
+// units pull the weight, not by HBM: at batch 1 a conv site's 640 coefficients (6.5 MB of
+// weight at width 5120) make only 40 workgroups of 16 features. When the output tiles
+// number fewer than the compute units, the contraction is also split over KS workgroups
+// (grid z) that write binary32 partials to the workspace, and a second kernel adds the KS
+// partials of each output in split order. Either way the sum's order is fixed.
 #include "common.hpp"
 
 namespace df2 {
@@ -35,19 +41,26 @@ constexpr int kPjRows = 16;   // output features per workgroup
 constexpr int kPjStep = 32;   // columns per MFMA
 constexpr int kPjPad = 17;    // LDS row pitch of a partial tile (floats)
 
+constexpr int kPjMaxSplit = 16;   // most contraction splits over workgroups
+constexpr int kPjTargetWGs = 256;  // one workgroup per compute unit
+
 template <int MT, int NS>
 __global__ __launch_bounds__(64 * kPjWaves) void proj_kernel(
     const uint16_t* __restrict__ hid, int64_t hss, int64_t hrs, int row0, int N, int M,
     const uint16_t* __restrict__ wt, int C, int O, float* __restrict__ out, int64_t oss,
-    int64_t ors) {
+    int64_t ors, float* __restrict__ part_out) {
   __shared__ float part[kPjWaves * 16 * MT * kPjPad];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int o0 = blockIdx.x * kPjRows;
   const int m0 = blockIdx.y * (16 * MT);
+  // this workgroup's share of the 32-column steps (split blockIdx.z of gridDim.z), then
+  // wave w's contiguous part of it
   const int steps = (C + kPjStep - 1) / kPjStep;
-  const int sb = (int)((int64_t)steps * w / kPjWaves);
-  const int se = (int)((int64_t)steps * (w + 1) / kPjWaves);
+  const int gb = (int)((int64_t)steps * blockIdx.z / gridDim.z);
+  const int ge = (int)((int64_t)steps * (blockIdx.z + 1) / gridDim.z);
+  const int sb = gb + (int)((int64_t)(ge - gb) * w / kPjWaves);
+  const int se = gb + (int)((int64_t)(ge - gb) * (w + 1) / kPjWaves);
 
   // rows past O or M are clamped to the last one (their results are never written)
   const uint16_t* wrow = wt + (int64_t)min(o0 + r, O - 1) * C;
@@ -72,20 +85,22 @@ __global__ __launch_bounds__(64 * kPjWaves) void proj_kernel(
     for (int s = 0; s < NS; ++s) {
       const int c = (s0 + s) * kPjStep + 8 * g;
       // C % 8 == 0, so a piece that starts inside the row ends inside it
+      // lanes past the range issue no load (their operands are zero)
       ok[s] = (s0 + s < se) && (c < C);
-      const int cl = ok[s] ? c : 0;
-      a[s] = *reinterpret_cast<const u32x4_t*>(wrow + cl);
+      a[s] = zero;
+      if (ok[s]) a[s] = *reinterpret_cast<const u32x4_t*>(wrow + c);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) bv[mt][s] = *reinterpret_cast<const u32x4_t*>(hrow[mt] + cl);
+      for (int mt = 0; mt < MT; ++mt) {
+        bv[mt][s] = zero;
+        if (ok[s]) bv[mt][s] = *reinterpret_cast<const u32x4_t*>(hrow[mt] + c);
+      }
     }
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const u32x4_t av = ok[s] ? a[s] : zero;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const u32x4_t hv = ok[s] ? bv[mt][s] : zero;
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                          __builtin_bit_cast(bf16x8_t, hv),
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[s]),
+                                                          __builtin_bit_cast(bf16x8_t, bv[mt][s]),
                                                           acc[mt], 0, 0, 0);
       }
     }
@@ -106,10 +121,52 @@ __global__ __launch_bounds__(64 * kPjWaves) void proj_kernel(
     for (int v = 1; v < kPjWaves; ++v) s = __fadd_rn(s, part[(v * 16 * MT + ml) * kPjPad + ol]);
     const int m = m0 + ml, o = o0 + ol;
     if (m < M && o < O) {
-      const int b = m / N, rr = m - b * N;
-      out[(int64_t)b * oss + (int64_t)rr * ors + o] = s;
+      if (part_out) {
+        part_out[((int64_t)blockIdx.z * M + m) * O + o] = s;
+      } else {
+        const int b = m / N, rr = m - b * N;
+        out[(int64_t)b * oss + (int64_t)rr * ors + o] = s;
+      }
     }
   }
+}
+
+// out[m, o] = sum over splits k in order of part[k, m, o]; every load is issued first
+__global__ __launch_bounds__(256) void proj_reduce_kernel(const float* __restrict__ part, int KS,
+                                                          int M, int O, int N,
+                                                          float* __restrict__ out, int64_t oss,
+                                                          int64_t ors) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t MO = (int64_t)M * O;
+  if (e >= MO) return;
+  float v[kPjMaxSplit];
+#pragma unroll
+  for (int k = 0; k < kPjMaxSplit; ++k) v[k] = k < KS ? part[k * MO + e] : 0.0f;
+  float s = v[0];
+#pragma unroll
+  for (int k = 1; k < kPjMaxSplit; ++k)
+    if (k < KS) s = __fadd_rn(s, v[k]);
+  const int m = (int)(e / O), o = (int)(e - (int64_t)m * O);
+  const int b = m / N, rr = m - b * N;
+  out[(int64_t)b * oss + (int64_t)rr * ors + o] = s;
+}
+
+struct ProjPlan {
+  int mt;  // row tiles of 16 per workgroup
+  int ks;  // contraction splits over workgroups
+};
+
+ProjPlan plan_proj(int M, int O, int C) {
+  ProjPlan p;
+  p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  const int64_t tiles = (int64_t)((O + kPjRows - 1) / kPjRows) * ((M + 16 * p.mt - 1) / (16 * p.mt));
+  const int steps = (C + kPjStep - 1) / kPjStep;
+  int ks = (int)((kPjTargetWGs + tiles - 1) / tiles);
+  const int by_steps = steps / kPjWaves;  // at least one step per wave
+  ks = ks < by_steps ? ks : by_steps;
+  ks = ks < kPjMaxSplit ? ks : kPjMaxSplit;
+  p.ks = ks < 1 ? 1 : ks;
+  return p;
 }
 
 }  // namespace
@@ -117,9 +174,18 @@ __global__ __launch_bounds__(64 * kPjWaves) void proj_kernel(
 
 using namespace df2;
 
+extern "C" size_t dflash2_proj_workspace_bytes(int B, int N, int O, int C) {
+  if (B < 1 || N < 1 || O < 1 || C < 1 || (int64_t)B * N > (1 << 20) || O > (1 << 26)) return 0;
+  const int M = B * N;
+  const ProjPlan p = plan_proj(M, O, C);
+  if (p.ks == 1) return 0;
+  return round_up((size_t)p.ks * M * O * sizeof(float), kWsAlign);
+}
+
 extern "C" int dflash2_proj(const void* hidden, int64_t hid_seq_stride, int64_t hid_row_stride,
                             int row0, const void* weight, int C, int O, int B, int N, float* out,
-                            int64_t out_seq_stride, int64_t out_row_stride, hipStream_t stream) {
+                            int64_t out_seq_stride, int64_t out_row_stride, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
   if (!hidden || !weight || !out) return DFLASH2_EINVAL;
   if (B < 1 || N < 1 || row0 < 0 || C < 1 || O < 1 || hid_seq_stride < 0 || hid_row_stride < 0)
     return DFLASH2_EINVAL;
@@ -137,21 +203,46 @@ extern "C" int dflash2_proj(const void* hidden, int64_t hid_seq_stride, int64_t 
   if (!aligned(hidden, 16) || !aligned(weight, 16) || hid_seq_stride % 8 != 0 ||
       hid_row_stride % 8 != 0)
     return DFLASH2_EUNSUPPORTED;
+  const size_t need = dflash2_proj_workspace_bytes(B, N, O, C);
+  if (need && (!ws || !aligned(ws, kWsAlign) || ws_bytes < need)) return DFLASH2_EWORKSPACE;
   const int M = B * N;
+  const ProjPlan p = plan_proj(M, O, C);
+  float* part = p.ks > 1 ? (float*)ws : nullptr;
   const int gx = (O + kPjRows - 1) / kPjRows;
+  const int gy = (M + 16 * p.mt - 1) / (16 * p.mt);
+  const dim3 grid(gx, gy, p.ks);
+  // steps per wave: at most ceil(ceil(C / 32) / ks / 8)
+  const int per_wave = (((C + kPjStep - 1) / kPjStep + p.ks - 1) / p.ks + kPjWaves - 1) / kPjWaves;
+  const uint16_t* h = (const uint16_t*)hidden;
+  const uint16_t* wt = (const uint16_t*)weight;
   const hipStream_t st = stream;
-  if (M <= 16) {
-    proj_kernel<1, 20><<<dim3(gx, 1), 64 * kPjWaves, 0, st>>>(
-        (const uint16_t*)hidden, hid_seq_stride, hid_row_stride, row0, N, M,
-        (const uint16_t*)weight, C, O, out, out_seq_stride, out_row_stride);
-  } else if (M <= 32) {
-    proj_kernel<2, 12><<<dim3(gx, 1), 64 * kPjWaves, 0, st>>>(
-        (const uint16_t*)hidden, hid_seq_stride, hid_row_stride, row0, N, M,
-        (const uint16_t*)weight, C, O, out, out_seq_stride, out_row_stride);
+  if (p.mt == 1) {
+    if (per_wave <= 4)
+      proj_kernel<1, 4><<<grid, 64 * kPjWaves, 0, st>>>(h, hid_seq_stride, hid_row_stride, row0,
+                                                         N, M, wt, C, O, out, out_seq_stride,
+                                                         out_row_stride, part);
+    else
+      proj_kernel<1, 20><<<grid, 64 * kPjWaves, 0, st>>>(h, hid_seq_stride, hid_row_stride, row0,
+                                                          N, M, wt, C, O, out, out_seq_stride,
+                                                          out_row_stride, part);
+  } else if (p.mt == 2) {
+    if (per_wave <= 4)
+      proj_kernel<2, 4><<<grid, 64 * kPjWaves, 0, st>>>(h, hid_seq_stride, hid_row_stride, row0,
+                                                         N, M, wt, C, O, out, out_seq_stride,
+                                                         out_row_stride, part);
+    else
+      proj_kernel<2, 12><<<grid, 64 * kPjWaves, 0, st>>>(h, hid_seq_stride, hid_row_stride, row0,
+                                                          N, M, wt, C, O, out, out_seq_stride,
+                                                          out_row_stride, part);
   } else {
-    proj_kernel<4, 8><<<dim3(gx, (M + 63) / 64), 64 * kPjWaves, 0, st>>>(
-        (const uint16_t*)hidden, hid_seq_stride, hid_row_stride, row0, N, M,
-        (const uint16_t*)weight, C, O, out, out_seq_stride, out_row_stride);
+    proj_kernel<4, 8><<<grid, 64 * kPjWaves, 0, st>>>(h, hid_seq_stride, hid_row_stride, row0, N,
+                                                       M, wt, C, O, out, out_seq_stride,
+                                                       out_row_stride, part);
+  }
+  if (p.ks > 1) {
+    const int64_t MO = (int64_t)M * O;
+    proj_reduce_kernel<<<(unsigned)((MO + 255) / 256), 256, 0, st>>>(
+        part, p.ks, M, O, N, out, out_seq_stride, out_row_stride);
   }
   return launch_status();
 }

@@ -46,7 +46,8 @@ SIGNATURES = {
     "dflash2_topk16_workspace_bytes": ([_i32] * 4, _sz),
     "dflash2_lmhead_topk16": ([_vp, _i64, _i64, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp], _i32),
     "dflash2_lmhead_topk16_workspace_bytes": ([_i32] * 4, _sz),
-    "dflash2_proj": ([_vp, _i64, _i64, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _i64, _i64, _vp], _i32),
+    "dflash2_proj": ([_vp, _i64, _i64, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _i64, _i64, _vp, _sz, _vp], _i32),
+    "dflash2_proj_workspace_bytes": ([_i32] * 4, _sz),
     "dflash2_select": ([_vp] * 5 + [_i32, _i32, _vp, _vp, _u64, _u64, _i32, _i32] + [_vp] * 5 + [_sz, _vp], _i32),
     "dflash2_select_workspace_bytes": ([_i32] * 2, _sz),
     "dflash2_ddtree": ([_vp] * 5 + [_i32, _i32, _vp, _i32, _i32, _i32] + [_vp] * 7 + [_sz, _vp], _i32),
@@ -218,8 +219,12 @@ def lmhead_topk16(hidden, B, N, row0, seq_stride, row_stride, weight, idx=None, 
     return idx, val
 
 
+def proj_workspace_bytes(B, N, O, C) -> int:
+    return int(_lib.dflash2_proj_workspace_bytes(B, N, O, C))
+
+
 def proj(hidden, B, N, row0, seq_stride, row_stride, weight, out=None, out_seq_stride=None,
-         out_row_stride=None, stream=None):
+         out_row_stride=None, ws=None, stream=None):
     """out[b, r, o] = sum_c hidden[b*seq_stride + (row0+r)*row_stride + c] * weight[o, c] in
     binary32; hidden bf16 rows addressed by element strides, weight bf16 [O, C]. With no
     out given, a new f32 [B, N, O] tensor."""
@@ -238,8 +243,12 @@ def proj(hidden, B, N, row0, seq_stride, row_stride, weight, out=None, out_seq_s
         if out_seq_stride is None or out_row_stride is None:
             _contig(out)
             out_seq_stride, out_row_stride = N * O, O
+    need = proj_workspace_bytes(B, N, O, C)
+    if ws is None and need:
+        ws = workspace(need, hidden.device)
     rc = _lib.dflash2_proj(_ptr(hidden), seq_stride, row_stride, row0, _ptr(weight), C, O, B, N,
-                           _ptr(out), out_seq_stride, out_row_stride, _stream(stream))
+                           _ptr(out), out_seq_stride, out_row_stride, _ptr(ws),
+                           0 if ws is None else ws.numel(), _stream(stream))
     _check(rc, "dflash2_proj")
     return out
 

@@ -184,11 +184,15 @@ size_t dflash2_lmhead_topk16_workspace_bytes(int B, int N, int V, int C);
  * dflash2_dynconv2 takes delta (one call per half, weight offset by 2G*C). Selector gate:
  * weight [R, C], rows row0 = 1 .. N of the block, out [B, N, R]. Requires C % 8 == 0,
  * 16-byte aligned hidden and weight, hidden strides multiples of 8, B*N <= 2^20,
- * O <= 2^26. No workspace.
+ * O <= 2^26. Workspace: dflash2_proj_workspace_bytes (0 when the call needs none; then ws
+ * may be null). Small calls split the contraction over workgroups and add the partials
+ * there in a fixed order.
  */
 int dflash2_proj(const void *hidden, int64_t hid_seq_stride, int64_t hid_row_stride, int row0,
                  const void *weight, int C, int O, int B, int N, float *out,
-                 int64_t out_seq_stride, int64_t out_row_stride, hipStream_t stream);
+                 int64_t out_seq_stride, int64_t out_row_stride, void *ws, size_t ws_bytes,
+                 hipStream_t stream);
+size_t dflash2_proj_workspace_bytes(int B, int N, int O, int C);
 
 /*
  * dflash2_ring_update - keeps a drafter context ring in step with the committed sequence

@@ -246,8 +246,8 @@ def test_proj_rejects():
     L = d2.lib()
 
     def call(hid=FAKE, w=FAKE, C=5120, O=640, B=2, N=8, row0=0, ss=8 * 5120, rs=5120,
-             out=FAKE, oss=8 * 640, ors=640):
-        return L.dflash2_proj(hid, ss, rs, row0, w, C, O, B, N, out, oss, ors, None)
+             out=FAKE, oss=8 * 640, ors=640, ws=FAKE, wsb=1 << 30):
+        return L.dflash2_proj(hid, ss, rs, row0, w, C, O, B, N, out, oss, ors, ws, wsb, None)
     assert call(hid=NUL) == d2.EINVAL
     assert call(out=NUL) == d2.EINVAL
     assert call(B=0) == d2.EINVAL
@@ -260,3 +260,7 @@ def test_proj_rejects():
     assert call(rs=5121) == d2.EUNSUPPORTED            # row stride not a multiple of 8
     assert call(w=ctypes.c_void_p(0x100008)) == d2.EUNSUPPORTED
     assert call(B=1 << 18, N=8) == d2.EUNSUPPORTED     # more than 2^20 rows
+    assert call(wsb=16) == d2.EWORKSPACE               # small call: split contraction
+    assert call(ws=NUL) == d2.EWORKSPACE
+    assert d2.proj_workspace_bytes(2, 8, 640, 5120) > 0
+    assert d2.proj_workspace_bytes(64, 8, 640, 5120) == 0   # enough output tiles already
