@@ -62,6 +62,29 @@ def set_bytes(cfg):
     return ring + logits + conv
 
 
+def stage_bytes(cfg, n_accept_sets):
+    """Algorithmic bytes per call of each stage other than attention (what the method must
+    move): conv reads x and writes out once, plus the coefficients and the base; top-16
+    reads the N ranked logits rows once and writes the lists; the selector gathers the
+    anchor's and each slot's predecessor rows of A and the slots' candidate rows of B,
+    reads the gates and candidates; verify reads, per greedy sequence, the n + 1 target
+    rows the argmax chain needs, and per sampled sequence the one row it draws from.
+    n_accept_sets: the accept counts of each input set's step."""
+    esz = 2 if cfg.act_bf16 else 4
+    tsz = 4 if cfg.target_kind == "probs" else esz
+    G = cfg.C // 16
+    B, P, N, V, R = cfg.B, cfg.P, cfg.N, cfg.V, cfg.R
+    conv = 2 * B * P * cfg.C * esz + B * P * 2 * G * 4 + 2 * cfg.C * 4
+    topk = B * N * V * esz + B * N * 16 * 8
+    select = B * ((1 + (N - 1) * 16 + N * 16) * R * 2 + N * R * 4 + N * 16 * 8)
+    temps = cfg.temperatures()
+    ver = []
+    for n_acc in n_accept_sets:
+        rows = sum(1 if temps[b] > 0 else int(n_acc[b]) + 1 for b in range(B))
+        ver.append(rows * V * tsz + B * N * 16 * 8)
+    return {"dynconv2": conv, "topk16": topk, "select": select, "verify": sum(ver) / len(ver)}
+
+
 def traffic_record(workload):
     """HBM bytes per attention launch from the committed PMC summary, if it was taken on
     the current kernel source."""
@@ -250,6 +273,13 @@ def main():
                 "topk16": timed(topk_call, reps), "select": timed(select_call, reps),
                 "verify": timed(verify_call, reps)}
     attn_ms = stage_ms["block_attn"]
+    # accept counts of every input set's step (the verify timing graph rotates the sets)
+    n_acc_sets = []
+    for i in range(nsets):
+        runner.run(i, i)
+        n_acc_sets.append(o.n_accept.cpu().numpy().copy())
+    runner.run(0, 0)
+    torch.cuda.synchronize()
     # the timing graph visits every input set equally often: average their byte counts
     per_set = [attn_bytes_flops(cfg, x.ctx_len.cpu().numpy()) for x in inputs]
     a_bytes = sum(p[0] for p in per_set) / len(per_set)
@@ -257,6 +287,12 @@ def main():
     achieved = a_bytes / (attn_ms * 1e-3) / 1e9
     traffic = traffic_record(cfg.cfg)
     mean_acc = float(o.n_accept.float().mean().item())
+    sb = stage_bytes(cfg, n_acc_sets)
+    stage_hbm = {"block_attn": {"bytes_per_call": a_bytes, "achieved": achieved,
+                                "frac": achieved / HBM_PEAK_GBS}}
+    for k, nb in sb.items():
+        gbs = nb / (stage_ms[k] * 1e-3) / 1e9
+        stage_hbm[k] = {"bytes_per_call": float(nb), "achieved": gbs, "frac": gbs / HBM_PEAK_GBS}
 
     # The output-head projection fused with the top-16 (a call outside the step): the
     # drafter's rows 1..N against a synthetic V x C bf16 head, ~N(0, 1/C), generated on the
@@ -412,6 +448,7 @@ def main():
                      "mfma_tflops": a_flops / (attn_ms * 1e-3) / 1e12,
                      "mfma_frac": a_flops / (attn_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
         "stage_us": {k: v * 1e3 for k, v in stage_ms.items()},
+        "stage_hbm": stage_hbm,
         "step_event_ms": ev_ms / args.steps,
         "ms_per_step_host_sync": ms_sync,
         "mean_accepted": mean_acc,

@@ -65,29 +65,33 @@ __device__ __forceinline__ uint32_t load_bits(const typename KT::elem_t* p, int6
 
 // Accept chain of a sampled sequence, computed by wave 0 (lane j-1 tests proposal j) and
 // published in *rec (LDS). All threads must call; returns after a barrier.
-// x and sl are lane t's proposal token and slot (loaded by the caller; t < N).
+// x and sl are lane t's proposal token and slot (loaded by the caller; t < N); allc/allq
+// hold the sequence's candidates and q ([N][16], LDS), written by the caller before the
+// call (the barrier on entry orders them).
 __device__ void accept_chain(const float* __restrict__ tgt, int64_t row_stride, int V, int N,
-                             int32_t x, int32_t sl, const int32_t* __restrict__ cidx,
-                             const float* __restrict__ q, uint64_t seed, uint64_t step, int b,
-                             ChainRec* rec) {
+                             int32_t x, int32_t sl, const int32_t* allc, const float* allq,
+                             uint64_t seed, uint64_t step, int b, ChainRec* rec) {
   const int t = threadIdx.x;
+  __syncthreads();
   if (t < 64) {
     bool acc = false, plain = false;
     int fl = 0;
     if (t < N) {
       const int j = t + 1;
+      // the target gather goes out first (at a clamped, always valid index)
+      const int xc = x < 0 ? 0 : (x >= V ? V - 1 : x);
+      const float pt_raw = tgt[(int64_t)t * row_stride + xc];
       Draw d = philox_draw(seed, step, (uint32_t)b, (uint32_t)j);
       const float u = uniform24(d.w[1]);
       if (x < 0 || x >= V) {
         plain = true;
       } else {
-        const int32_t* ci = cidx + ((int64_t)b * N + t) * kTopK;
-        if (sl < 0 || sl >= kTopK || ci[sl] != x) {
+        if (sl < 0 || sl >= kTopK || allc[t * kTopK + sl] != x) {
           fl |= DFLASH2_ST_BADTOKEN;
           plain = true;
         } else {
-          const float qx = prob_ok(q[((int64_t)b * N + t) * kTopK + sl], &fl);
-          const float pt = prob_ok(tgt[(int64_t)t * row_stride + x], &fl);
+          const float qx = prob_ok(allq[t * kTopK + sl], &fl);
+          const float pt = prob_ok(pt_raw, &fl);
           acc = __fmul_rn(u, qx) < pt;
         }
       }
@@ -179,10 +183,19 @@ __global__ __launch_bounds__(kThreads) void verify_rows_kernel(
   __shared__ int redf[kThreads / 64];
 
   // a sampled chain's first loads do not depend on the temperature: issue them with it
+  // (the proposals and slots, and on an f32 target every slot's candidates and q)
+  __shared__ int32_t allc[kMaxN * kTopK];
+  __shared__ float allq[kMaxN * kTopK];
   int32_t x_pre = -1, sl_pre = -1;
   if (t < N) {
     x_pre = tokens[(int64_t)b * N + t];
     sl_pre = slot[(int64_t)b * N + t];
+  }
+  int32_t ci_pre = -1;
+  float q_pre = 0.0f;
+  if (sizeof(typename KT::elem_t) == 4 && t < N * kTopK) {
+    ci_pre = cidx[(int64_t)b * N * kTopK + t];
+    q_pre = q[(int64_t)b * N * kTopK + t];
   }
   int st = 0;
   float invT = 0.0f;
@@ -231,7 +244,11 @@ __global__ __launch_bounds__(kThreads) void verify_rows_kernel(
 
   // sampled: which row, and with which candidate corrections
   const float* tgt = reinterpret_cast<const float*>(tb);
-  accept_chain(tgt, row_stride, V, N, x_pre, sl_pre, cidx, q, seed, step, b, &rec);
+  if (t < N * kTopK) {
+    allc[t] = ci_pre;
+    allq[t] = q_pre;
+  }
+  accept_chain(tgt, row_stride, V, N, x_pre, sl_pre, allc, allq, seed, step, b, &rec);
   if (chunk == 0 && t == 0) ws.chain[b] = rec;
   const float* row = tgt + (int64_t)(rec.pos - 1) * row_stride;
 
@@ -251,15 +268,16 @@ __global__ __launch_bounds__(kThreads) void verify_rows_kernel(
   // repeated index only its first occurrence counts
   int64_t dz = 0;
   if (rec.resid && t < kTopK) {
-    const int32_t* ci = cidx + ((int64_t)b * N + (rec.pos - 1)) * kTopK;
-    const float* qr = q + ((int64_t)b * N + (rec.pos - 1)) * kTopK;
+    const int32_t* ci = allc + (rec.pos - 1) * kTopK;
     const int32_t c = ci[t];
     bool first = c >= 0 && c < V;
-    for (int k = 0; k < t; ++k) first = first && ci[k] != c;
+#pragma unroll
+    for (int k = 0; k < kTopK; ++k)
+      if (k < t) first = first && ci[k] != c;
     if (first && c >= base && c < base + CH) {
       int dummy = 0;
       const float p = prob_ok(row[c], &dummy);
-      const float qk = prob_ok(qr[t], &fl);
+      const float qk = prob_ok(allq[(rec.pos - 1) * kTopK + t], &fl);
       const float d = __fsub_rn(p, qk);
       dz = (int64_t)quant40(d > 0.0f ? d : 0.0f) - (int64_t)quant40(p);
     }
@@ -323,6 +341,8 @@ __global__ __launch_bounds__(kThreads) void verify_finish_kernel(
   __shared__ int sh_tok;
   __shared__ int32_t cand[kTopK];
   __shared__ float candq[kTopK];
+  __shared__ int32_t allc[kMaxN * kTopK];
+  __shared__ float allq[kMaxN * kTopK];
 
   // The greedy chain's chunk maxima are loaded before the temperature is known (for up to
   // 128 chunks: wave w takes rows w, w + 4, ..., lane l chunks l and l + 64), so that the
@@ -341,10 +361,35 @@ __global__ __launch_bounds__(kThreads) void verify_finish_kernel(
       for (int i = 0; i < 2; ++i) pre[j][i] = src[min(lane + 64 * i, nchunks - 1)];
     }
   }
+  constexpr bool kIsF32 = sizeof(typename KT::elem_t) == 4;
+  // A sampled sequence's inputs do not depend on the temperature either: the chain record,
+  // this thread's chunk sums (chunks t*cpt .. t*cpt + cpt - 1, kept in registers for up to
+  // kCptMax chunks) and every slot's candidates, loaded in the same round trip. The
+  // workspace holds these arrays for either target type; a greedy sequence ignores them.
+  constexpr int kCptMax = 4;
+  const int cpt = (nchunks + kThreads - 1) / kThreads;
+  ChainRec rec_pre = {0, 1, 0, 0};
+  uint64_t zr_pre[kCptMax], zp_pre[kCptMax];
+  int zf_pre[kCptMax];
+  int32_t ci_pre = -1;
+  float q_pre = 0.0f;
+  if constexpr (kIsF32) {
+    rec_pre = ws.chain[b];
+#pragma unroll
+    for (int i = 0; i < kCptMax; ++i) {
+      const int c = min(t * cpt + i, nchunks - 1);
+      zr_pre[i] = ws.zsum[((int64_t)b * nchunks + c) * 2 + 0];
+      zp_pre[i] = ws.zsum[((int64_t)b * nchunks + c) * 2 + 1];
+      zf_pre[i] = ws.zflag[(int64_t)b * nchunks + c];
+    }
+    if (t < N * kTopK) {
+      ci_pre = cidx[(int64_t)b * N * kTopK + t];
+      q_pre = q[(int64_t)b * N * kTopK + t];
+    }
+  }
   int st = 0;
   float invT = 0.0f;
   int mode = temp_mode(temperature[b], &invT, &st);
-  constexpr bool kIsF32 = sizeof(typename KT::elem_t) == 4;
   if (mode == 1 && !kIsF32) {
     st |= DFLASH2_ST_BADPROB;
     mode = 0;
@@ -397,21 +442,35 @@ __global__ __launch_bounds__(kThreads) void verify_finish_kernel(
   }
 
   // sampled
-  const ChainRec rec = ws.chain[b];
+  const ChainRec rec = rec_pre;
   st |= rec.flags;
   const float* row = reinterpret_cast<const float*>(tb) + (int64_t)(rec.pos - 1) * row_stride;
+  if (t < N * kTopK) {
+    allc[t] = ci_pre;
+    allq[t] = q_pre;
+  }
   // thread t owns chunks t*cpt .. t*cpt + cpt - 1 (in index order), so a workgroup scan of
   // the per-thread sums finds the chunk that holds the draw
-  const int cpt = (nchunks + kThreads - 1) / kThreads;
   uint64_t my_zr = 0, my_zp = 0;
   {
     int f = 0;
-    for (int i = 0; i < cpt; ++i) {
-      const int c = t * cpt + i;
-      if (c < nchunks) {
-        my_zr += ws.zsum[((int64_t)b * nchunks + c) * 2 + 0];
-        my_zp += ws.zsum[((int64_t)b * nchunks + c) * 2 + 1];
-        f |= ws.zflag[(int64_t)b * nchunks + c];
+    if (cpt <= kCptMax) {
+#pragma unroll
+      for (int i = 0; i < kCptMax; ++i) {
+        if (i < cpt && t * cpt + i < nchunks) {
+          my_zr += zr_pre[i];
+          my_zp += zp_pre[i];
+          f |= zf_pre[i];
+        }
+      }
+    } else {
+      for (int i = 0; i < cpt; ++i) {
+        const int c = t * cpt + i;
+        if (c < nchunks) {
+          my_zr += ws.zsum[((int64_t)b * nchunks + c) * 2 + 0];
+          my_zp += ws.zsum[((int64_t)b * nchunks + c) * 2 + 1];
+          f |= ws.zflag[(int64_t)b * nchunks + c];
+        }
       }
     }
     const uint64_t zr = wave_sum_u64(my_zr);
@@ -445,9 +504,10 @@ __global__ __launch_bounds__(kThreads) void verify_finish_kernel(
     Z = sh_z[1];
   }
   if (t < kTopK) {
+    // the barriers above ordered the allc/allq writes before these reads
     if (use_resid) {
-      cand[t] = cidx[((int64_t)b * N + (rec.pos - 1)) * kTopK + t];
-      candq[t] = q[((int64_t)b * N + (rec.pos - 1)) * kTopK + t];
+      cand[t] = allc[(rec.pos - 1) * kTopK + t];
+      candq[t] = allq[(rec.pos - 1) * kTopK + t];
     } else {
       cand[t] = -1;
       candq[t] = 0.0f;
@@ -487,10 +547,21 @@ __global__ __launch_bounds__(kThreads) void verify_finish_kernel(
     if (excl_z <= tau_all && tau_all < incl_z) {
       uint64_t cum = excl_z;
       int c = t * cpt;
-      for (int i = 0; i < cpt && c < nchunks; ++i, ++c) {
-        const uint64_t zc = ws.zsum[((int64_t)b * nchunks + c) * 2 + (use_resid ? 0 : 1)];
-        if (cum + zc > tau_all) break;
-        cum += zc;
+      if (cpt <= kCptMax) {
+#pragma unroll
+        for (int i = 0; i < kCptMax; ++i) {
+          if (i >= cpt || c >= nchunks) break;
+          const uint64_t zc = use_resid ? zr_pre[i] : zp_pre[i];
+          if (cum + zc > tau_all) break;
+          cum += zc;
+          ++c;
+        }
+      } else {
+        for (int i = 0; i < cpt && c < nchunks; ++i, ++c) {
+          const uint64_t zc = ws.zsum[((int64_t)b * nchunks + c) * 2 + (use_resid ? 0 : 1)];
+          if (cum + zc > tau_all) break;
+          cum += zc;
+        }
       }
       sh_chunk = c;
       sh_tau = tau_all - cum;
@@ -501,19 +572,30 @@ __global__ __launch_bounds__(kThreads) void verify_finish_kernel(
     uint64_t wgt[EPT];
     uint64_t mine = 0;
     int dummy = 0;
+    float pv[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) pv[e] = c0 + e < V ? row[c0 + e] : 0.0f;
+    int32_t ck[kTopK];
+    float qk[kTopK];
+#pragma unroll
+    for (int k = 0; k < kTopK; ++k) {
+      ck[k] = cand[k];
+      qk[k] = candq[k];
+    }
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
       const int x = c0 + e;
       uint64_t r = 0;
       if (x < V) {
-        const float p = prob_ok(row[x], &dummy);
+        const float p = prob_ok(pv[e], &dummy);
         r = quant40(p);
-        for (int k = 0; k < kTopK; ++k) {
-          if (cand[k] == x) {
-            const float qk = prob_ok(candq[k], &dummy);
-            const float df = __fsub_rn(p, qk);
+        // a candidate index replaces the weight by the residual; for a repeated index
+        // the first occurrence counts, so the candidates are applied last to first
+#pragma unroll
+        for (int k = kTopK - 1; k >= 0; --k) {
+          if (ck[k] == x) {
+            const float df = __fsub_rn(p, prob_ok(qk[k], &dummy));
             r = quant40(df > 0.0f ? df : 0.0f);
-            break;
           }
         }
       }
