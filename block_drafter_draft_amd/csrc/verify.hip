@@ -257,16 +257,10 @@ __global__ __launch_bounds__(kThreads) void verify_rows_kernel(
     load_chunk_full<KT, EPT>(reinterpret_cast<const typename KT::elem_t*>(row), base, bits);
   else
     load_chunk<KT, EPT, VEC>(reinterpret_cast<const typename KT::elem_t*>(row), base, V, bits);
-  uint64_t zp = 0;
-  int fl = 0;
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    const int x = index_of<EPT, VEC, KT>(base, e);
-    if (x < V) zp += quant40(prob_ok(__uint_as_float(bits[e]), &fl));
-  }
   // residual corrections for the candidates of slot pos that fall in this chunk; for a
-  // repeated index only its first occurrence counts
-  int64_t dz = 0;
+  // repeated index only its first occurrence counts. Their gathers go out with the chunk.
+  bool corr = false;
+  float p_c = 0.0f, q_c = 0.0f;
   if (rec.resid && t < kTopK) {
     const int32_t* ci = allc + (rec.pos - 1) * kTopK;
     const int32_t c = ci[t];
@@ -275,12 +269,25 @@ __global__ __launch_bounds__(kThreads) void verify_rows_kernel(
     for (int k = 0; k < kTopK; ++k)
       if (k < t) first = first && ci[k] != c;
     if (first && c >= base && c < base + CH) {
-      int dummy = 0;
-      const float p = prob_ok(row[c], &dummy);
-      const float qk = prob_ok(allq[(rec.pos - 1) * kTopK + t], &fl);
-      const float d = __fsub_rn(p, qk);
-      dz = (int64_t)quant40(d > 0.0f ? d : 0.0f) - (int64_t)quant40(p);
+      corr = true;
+      p_c = row[c];
+      q_c = allq[(rec.pos - 1) * kTopK + t];
     }
+  }
+  uint64_t zp = 0;
+  int fl = 0;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int x = index_of<EPT, VEC, KT>(base, e);
+    if (x < V) zp += quant40(prob_ok(__uint_as_float(bits[e]), &fl));
+  }
+  int64_t dz = 0;
+  if (corr) {
+    int dummy = 0;
+    const float p = prob_ok(p_c, &dummy);
+    const float qk = prob_ok(q_c, &fl);
+    const float d = __fsub_rn(p, qk);
+    dz = (int64_t)quant40(d > 0.0f ? d : 0.0f) - (int64_t)quant40(p);
   }
   uint64_t zr = zp + (uint64_t)dz;
   zp = wave_sum_u64(zp);
