@@ -41,7 +41,7 @@ constexpr int kPjRows = 16;   // output features per workgroup
 constexpr int kPjStep = 32;   // columns per MFMA
 constexpr int kPjPad = 17;    // LDS row pitch of a partial tile (floats)
 
-constexpr int kPjMaxSplit = 16;   // most contraction splits over workgroups
+constexpr int kPjMaxSplit = 32;   // most contraction splits over workgroups
 constexpr int kPjTargetWGs = 256;  // one workgroup per compute unit
 
 template <int MT, int NS>
@@ -131,6 +131,102 @@ __global__ __launch_bounds__(64 * kPjWaves) void proj_kernel(
   }
 }
 
+// More than 32 hidden rows: a workgroup of 4 waves owns a 64 x 64 tile (64 features x 64
+// rows) and each wave computes all 16 MFMA tiles of it over its quarter of the
+// contraction, so every operand fragment it loads feeds four products. Per step a lane
+// loads four weight pieces and four hidden pieces (columns 32 s + 8 g .. + 8 of rows
+// 16 t + r). This reads the hidden rows once per 64 features instead of once per 16:
+// about 105 MB instead of 262 MB of L2 traffic at batch 64 (512 rows, 640 features).
+constexpr int kTlWaves = 4;
+constexpr int kTlPad = 65;  // LDS row pitch (floats) of a 64 x 64 partial tile
+
+template <int NS>
+__global__ __launch_bounds__(64 * kTlWaves) void proj_tile_kernel(
+    const uint16_t* __restrict__ hid, int64_t hss, int64_t hrs, int row0, int N, int M,
+    const uint16_t* __restrict__ wt, int C, int O, float* __restrict__ out, int64_t oss,
+    int64_t ors, float* __restrict__ part_out) {
+  __shared__ float part[kTlWaves * 64 * kTlPad];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int o0 = blockIdx.x * 64;
+  const int m0 = blockIdx.y * 64;
+  const int steps = (C + kPjStep - 1) / kPjStep;
+  const int gb = (int)((int64_t)steps * blockIdx.z / gridDim.z);
+  const int ge = (int)((int64_t)steps * (blockIdx.z + 1) / gridDim.z);
+  const int sb = gb + (int)((int64_t)(ge - gb) * w / kTlWaves);
+  const int se = gb + (int)((int64_t)(ge - gb) * (w + 1) / kTlWaves);
+
+  // rows past O or M are clamped to the last one (their results are never written)
+  const uint16_t* wrow[4];
+  const uint16_t* hrow[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    wrow[u] = wt + (int64_t)min(o0 + 16 * u + r, O - 1) * C;
+    const int m = min(m0 + 16 * u + r, M - 1);
+    const int b = m / N, rr = m - b * N;
+    hrow[u] = hid + (int64_t)b * hss + (int64_t)(row0 + rr) * hrs;
+  }
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+
+  for (int s0 = sb; s0 < se; s0 += NS) {
+    u32x4_t a[NS][4], bv[NS][4];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int c = (s0 + s) * kPjStep + 8 * g;
+      const bool ok = (s0 + s < se) && (c < C);  // C % 8 == 0: a piece is wholly inside
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        a[s][u] = zero;
+        bv[s][u] = zero;
+        if (ok) {
+          a[s][u] = *reinterpret_cast<const u32x4_t*>(wrow[u] + c);
+          bv[s][u] = *reinterpret_cast<const u32x4_t*>(hrow[u] + c);
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, a[s][i]), __builtin_bit_cast(bf16x8_t, bv[s][j]),
+              acc[i][j], 0, 0, 0);
+  }
+
+  // lane (r, g) of tile (i, j) holds feature 16 i + 4 g + e of row 16 j + r; LDS [o][m]
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        part[(w * 64 + 16 * i + 4 * g + e) * kTlPad + 16 * j + r] = acc[i][j][e];
+  __syncthreads();
+
+  for (int e = threadIdx.x; e < 64 * 64; e += 64 * kTlWaves) {
+    const int ml = e >> 6, ol = e & 63;
+    float sum = part[ol * kTlPad + ml];
+#pragma unroll
+    for (int v = 1; v < kTlWaves; ++v) sum = __fadd_rn(sum, part[(v * 64 + ol) * kTlPad + ml]);
+    const int m = m0 + ml, o = o0 + ol;
+    if (m < M && o < O) {
+      if (part_out) {
+        part_out[((int64_t)blockIdx.z * M + m) * O + o] = sum;
+      } else {
+        const int b = m / N, rr = m - b * N;
+        out[(int64_t)b * oss + (int64_t)rr * ors + o] = sum;
+      }
+    }
+  }
+}
+
 // out[m, o] = sum over splits k in order of part[k, m, o]; every load is issued first
 __global__ __launch_bounds__(256) void proj_reduce_kernel(const float* __restrict__ part, int KS,
                                                           int M, int O, int N,
@@ -152,17 +248,25 @@ __global__ __launch_bounds__(256) void proj_reduce_kernel(const float* __restric
 }
 
 struct ProjPlan {
-  int mt;  // row tiles of 16 per workgroup
-  int ks;  // contraction splits over workgroups
+  int mt;     // row tiles of 16 per workgroup (16-feature kernel)
+  bool tile;  // the 64 x 64 tile kernel instead
+  int ks;     // contraction splits over workgroups
 };
 
+// The tile kernel pays off once the hidden rows are re-read enough: measured from 256 rows,
+// or from 33 rows with at least 512 features (at 112 rows x 256 features the 16-feature
+// kernel is faster).
 ProjPlan plan_proj(int M, int O, int C) {
   ProjPlan p;
   p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-  const int64_t tiles = (int64_t)((O + kPjRows - 1) / kPjRows) * ((M + 16 * p.mt - 1) / (16 * p.mt));
+  p.tile = M >= 256 || (M > 32 && O >= 512);
+  const int orows = p.tile ? 64 : kPjRows;
+  const int waves = p.tile ? kTlWaves : kPjWaves;
+  const int mrows = p.tile ? 64 : 16 * p.mt;
+  const int64_t tiles = (int64_t)((O + orows - 1) / orows) * ((M + mrows - 1) / mrows);
   const int steps = (C + kPjStep - 1) / kPjStep;
   int ks = (int)((kPjTargetWGs + tiles - 1) / tiles);
-  const int by_steps = steps / kPjWaves;  // at least one step per wave
+  const int by_steps = steps / waves;  // at least one step per wave
   ks = ks < by_steps ? ks : by_steps;
   ks = ks < kPjMaxSplit ? ks : kPjMaxSplit;
   p.ks = ks < 1 ? 1 : ks;
@@ -208,15 +312,27 @@ extern "C" int dflash2_proj(const void* hidden, int64_t hid_seq_stride, int64_t 
   const int M = B * N;
   const ProjPlan p = plan_proj(M, O, C);
   float* part = p.ks > 1 ? (float*)ws : nullptr;
-  const int gx = (O + kPjRows - 1) / kPjRows;
-  const int gy = (M + 16 * p.mt - 1) / (16 * p.mt);
+  const int orows = p.tile ? 64 : kPjRows;
+  const int mrows = p.tile ? 64 : 16 * p.mt;
+  const int gx = (O + orows - 1) / orows;
+  const int gy = (M + mrows - 1) / mrows;
   const dim3 grid(gx, gy, p.ks);
-  // steps per wave: at most ceil(ceil(C / 32) / ks / 8)
-  const int per_wave = (((C + kPjStep - 1) / kPjStep + p.ks - 1) / p.ks + kPjWaves - 1) / kPjWaves;
+  // steps per wave: at most ceil(ceil(C / 32) / ks / waves)
+  const int waves = p.tile ? kTlWaves : kPjWaves;
+  const int per_wave = (((C + kPjStep - 1) / kPjStep + p.ks - 1) / p.ks + waves - 1) / waves;
   const uint16_t* h = (const uint16_t*)hidden;
   const uint16_t* wt = (const uint16_t*)weight;
   const hipStream_t st = stream;
-  if (p.mt == 1) {
+  if (p.tile) {
+    if (per_wave <= 2)
+      proj_tile_kernel<2><<<grid, 64 * kTlWaves, 0, st>>>(h, hid_seq_stride, hid_row_stride,
+                                                           row0, N, M, wt, C, O, out,
+                                                           out_seq_stride, out_row_stride, part);
+    else
+      proj_tile_kernel<4><<<grid, 64 * kTlWaves, 0, st>>>(h, hid_seq_stride, hid_row_stride,
+                                                           row0, N, M, wt, C, O, out,
+                                                           out_seq_stride, out_row_stride, part);
+  } else if (p.mt == 1) {
     if (per_wave <= 4)
       proj_kernel<1, 4><<<grid, 64 * kPjWaves, 0, st>>>(h, hid_seq_stride, hid_row_stride, row0,
                                                          N, M, wt, C, O, out, out_seq_stride,

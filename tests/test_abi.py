@@ -263,4 +263,4 @@ def test_proj_rejects():
     assert call(wsb=16) == d2.EWORKSPACE               # small call: split contraction
     assert call(ws=NUL) == d2.EWORKSPACE
     assert d2.proj_workspace_bytes(2, 8, 640, 5120) > 0
-    assert d2.proj_workspace_bytes(64, 8, 640, 5120) == 0   # enough output tiles already
+    assert d2.proj_workspace_bytes(256, 8, 640, 5120) == 0  # enough output tiles already

@@ -70,6 +70,8 @@ def check_bound(got, Y, A, C, what):
     (16, 7, 1, 256, 16, 0),       # the tiny configuration's gate shape
     (1, 1, 0, 8, 1, 0),           # smallest call
     (64, 8, 0, 5120, 640, 0),     # batch 64 at the drafter width
+    (256, 8, 0, 512, 640, 8),     # 2048 rows: enough 64 x 64 tiles for one kernel, no split
+    (5, 8, 0, 264, 520, 8),       # 64 x 64 tiles with ragged features, rows and contraction
 ])
 def test_proj_within_bound(d2, B, N, row0, C, O, pad):
     rng = np.random.default_rng(700 + B * 31 + C + O)
@@ -85,7 +87,8 @@ def test_proj_within_bound(d2, B, N, row0, C, O, pad):
     assert_same_floats(again, got, "a second call")
 
 
-@pytest.mark.parametrize("B,N,C,O", [(1, 8, 5120, 640), (7, 8, 264, 33), (3, 8, 1024, 48)])
+@pytest.mark.parametrize("B,N,C,O", [(1, 8, 5120, 640), (7, 8, 264, 33), (3, 8, 1024, 48),
+                                     (5, 8, 264, 520), (64, 8, 1024, 640)])
 def test_proj_exact_on_grid_data(d2, B, N, C, O):
     rng = np.random.default_rng(800 + B + C)
     hid = _grid(rng, (B * N * C,))
