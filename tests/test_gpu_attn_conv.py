@@ -204,3 +204,19 @@ def test_conv_shapes(d2, P, C):
     delta = rng.uniform(-1, 1, (B, P, 2, C // 16)).astype(np.float32)
     run_conv(d2, x, base, delta, f"f32 P{P} C{C}", dict(max_abs=1e-5, rel_l2=1e-6))
     run_conv(d2, wl.to_bf16_bits(x), base, delta, f"bf16 P{P} C{C}", BF16_TOL)
+
+
+@pytest.mark.parametrize("B,P,C", [(40, 16, 4096), (128, 3, 1024), (26, 8, 5120), (33, 1, 4000)])
+def test_conv_large_batches(d2, B, P, C):
+    # large batches (P up to 16, f32 and bf16, a ragged channel count): the same bounds,
+    # and identity taps reproduce the input exactly
+    rng = np.random.default_rng(90 + B + P)
+    x = rng.standard_normal((B, P, C)).astype(np.float32)
+    base = rng.uniform(-1, 1, (2, C)).astype(np.float32)
+    delta = rng.uniform(-1, 1, (B, P, 2, C // 16)).astype(np.float32)
+    run_conv(d2, x, base, delta, f"f32 large batch B{B} P{P} C{C}", dict(max_abs=1e-5, rel_l2=1e-6))
+    xb = wl.to_bf16_bits(x)
+    run_conv(d2, xb, base, delta, f"bf16 large batch B{B} P{P} C{C}", BF16_TOL)
+    ident = np.stack([np.ones(C), np.zeros(C)]).astype(np.float32)
+    got = run_conv(d2, xb, ident, np.zeros_like(delta), f"identity large batch B{B}", BF16_TOL)
+    np.testing.assert_array_equal(got, xb)
