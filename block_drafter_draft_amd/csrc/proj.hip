@@ -227,7 +227,9 @@ __global__ __launch_bounds__(64 * kTlWaves) void proj_tile_kernel(
   }
 }
 
-// out[m, o] = sum over splits k in order of part[k, m, o]; every load is issued first
+// out[m, o] = sum over splits k in order of part[k, m, o], KS <= KMAX. Every load is issued
+// first, unconditionally (splits past KS re-read the last one and are not added).
+template <int KMAX>
 __global__ __launch_bounds__(256) void proj_reduce_kernel(const float* __restrict__ part, int KS,
                                                           int M, int O, int N,
                                                           float* __restrict__ out, int64_t oss,
@@ -235,12 +237,12 @@ __global__ __launch_bounds__(256) void proj_reduce_kernel(const float* __restric
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t MO = (int64_t)M * O;
   if (e >= MO) return;
-  float v[kPjMaxSplit];
+  float v[KMAX];
 #pragma unroll
-  for (int k = 0; k < kPjMaxSplit; ++k) v[k] = k < KS ? part[k * MO + e] : 0.0f;
+  for (int k = 0; k < KMAX; ++k) v[k] = part[(k < KS ? k : KS - 1) * MO + e];
   float s = v[0];
 #pragma unroll
-  for (int k = 1; k < kPjMaxSplit; ++k)
+  for (int k = 1; k < KMAX; ++k)
     if (k < KS) s = __fadd_rn(s, v[k]);
   const int m = (int)(e / O), o = (int)(e - (int64_t)m * O);
   const int b = m / N, rr = m - b * N;
@@ -357,8 +359,19 @@ extern "C" int dflash2_proj(const void* hidden, int64_t hid_seq_stride, int64_t 
   }
   if (p.ks > 1) {
     const int64_t MO = (int64_t)M * O;
-    proj_reduce_kernel<<<(unsigned)((MO + 255) / 256), 256, 0, st>>>(
-        part, p.ks, M, O, N, out, out_seq_stride, out_row_stride);
+    const unsigned nb = (unsigned)((MO + 255) / 256);
+    if (p.ks <= 4)
+      proj_reduce_kernel<4><<<nb, 256, 0, st>>>(part, p.ks, M, O, N, out, out_seq_stride,
+                                                out_row_stride);
+    else if (p.ks <= 8)
+      proj_reduce_kernel<8><<<nb, 256, 0, st>>>(part, p.ks, M, O, N, out, out_seq_stride,
+                                                out_row_stride);
+    else if (p.ks <= 16)
+      proj_reduce_kernel<16><<<nb, 256, 0, st>>>(part, p.ks, M, O, N, out, out_seq_stride,
+                                                 out_row_stride);
+    else
+      proj_reduce_kernel<kPjMaxSplit><<<nb, 256, 0, st>>>(part, p.ks, M, O, N, out,
+                                                          out_seq_stride, out_row_stride);
   }
   return launch_status();
 }
