@@ -396,7 +396,15 @@ struct ElementValue {
   const typename KT::elem_t* scores;
   int64_t seq_stride, row_stride;
   int row0, N;
-  __device__ float operator()(int rowid, uint32_t x, uint32_t /*key*/) const {
+  // The lists hold canonical order keys, which give back the element's bits by undoing the
+  // sign-magnitude flip, except the NaN key (payload lost) and the zero key (sign lost):
+  // only those two read the element from the row.
+  __device__ float operator()(int rowid, uint32_t x, uint32_t key) const {
+    if (key != KT::kNaN && key != KT::kPosZero) {
+      constexpr uint32_t kSign = KT::kPosZero;  // the key's top bit: a non-negative element
+      const uint32_t mask = sizeof(typename KT::elem_t) == 2 ? 0xffffu : 0xffffffffu;
+      return KT::widen((key & kSign) ? (key ^ kSign) : (~key & mask));
+    }
     const int b = rowid / N, r = rowid % N;
     const typename KT::elem_t* row = scores + (int64_t)b * seq_stride + (int64_t)(row0 + r) * row_stride;
     uint32_t u;

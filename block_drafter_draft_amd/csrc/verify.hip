@@ -358,6 +358,8 @@ __global__ __launch_bounds__(kThreads) void verify_finish_kernel(
   uint64_t pre[kRowIt][2];
   __shared__ int32_t dtok[kMaxN];
   const int32_t my_tok = tokens[(int64_t)b * N + (t < N ? t : 0)];  // the proposals, with them
+  // the status word the selector left, read now so that the final update is a plain store
+  const int32_t st_in = t == 0 ? status[b] : 0;
   const bool few = nchunks <= 128;
   if (few) {
 #pragma unroll
@@ -443,7 +445,7 @@ __global__ __launch_bounds__(kThreads) void verify_finish_kernel(
       }
       for (int j = 0; j <= N; ++j) out[j] = j < n ? dtok[j] : (j == n ? emitted : -1);
       n_accept[b] = n;
-      status[b] |= st;
+      status[b] = st_in | st;
     }
     return;
   }
@@ -630,7 +632,7 @@ __global__ __launch_bounds__(kThreads) void verify_finish_kernel(
     const int n = rec.n_acc;
     for (int j = 0; j <= N; ++j) out[j] = j < n ? d[j] : (j == n ? emitted : -1);
     n_accept[b] = n;
-    status[b] |= st;
+    status[b] = st_in | st;
   }
 }
 
