@@ -179,3 +179,40 @@ def test_proj_gate_drives_the_selector(d2, T):
     np.testing.assert_array_equal(to_host(sl), o[1], err_msg="slot")
     assert_same_floats(to_host(q), o[2], "q")
     np.testing.assert_array_equal(to_host(st), o[3], err_msg="status")
+
+
+def test_proj_and_conv_replayed_in_a_graph(d2):
+    # the split path (workspace partials, then the ordered reduction) captured with the conv
+    # it feeds in one HIP graph; every replay, with the outputs scribbled over in between,
+    # must equal the eager result bit for bit
+    rng = np.random.default_rng(904)
+    B, P, C = 1, 8, 5120
+    G = C // 16
+    x = to_dev(_rand(rng, (B, P, C), 1.0))
+    w = to_dev(_rand(rng, (2 * G, C), C ** -0.5))
+    base = to_dev(rng.uniform(-1, 1, (2, C)).astype(np.float32))
+    delta = torch.empty((B, P, 2, G), dtype=torch.float32, device=x.device)
+    out = torch.empty((B, P, C), dtype=torch.bfloat16, device=x.device)
+    ws = d2.workspace(d2.proj_workspace_bytes(B, P, 2 * G, C), x.device)
+    assert d2.proj_workspace_bytes(B, P, 2 * G, C) > 0          # the split path
+    say("proj + dynconv2 graph replay B=1 C=5120")
+
+    def run():
+        d2.proj(x, B, P, 0, P * C, C, w, out=delta.view(B, P, 2 * G), ws=ws)
+        d2.dynconv2(x, base, delta, out=out)
+
+    run()
+    torch.cuda.synchronize()
+    want_d, want_o = to_host(delta), to_host(out)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(3):
+        delta.fill_(float("nan"))
+        out.view(torch.int16).fill_(-1)
+        ws.fill_(0xAB)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_same_floats(to_host(delta), want_d, f"coefficients, replay {rep}")
+        np.testing.assert_array_equal(to_host(out), want_o, err_msg=f"conv, replay {rep}")
