@@ -287,6 +287,14 @@ def main():
     achieved = a_bytes / (attn_ms * 1e-3) / 1e9
     traffic = traffic_record(cfg.cfg)
     mean_acc = float(o.n_accept.float().mean().item())
+    # The launch chain: kernel launches per step (attention is one kernel without splits,
+    # two with; top-16, select and verify are two each; conv one per site) and the per-node
+    # floor of a graph of one-element fills, the cheapest kernel node there is.
+    attn_k = 1 + (d2.block_attn_workspace_bytes(B, P, cfg.Hq, cfg.Hkv, cfg.D, cfg.S, cfg.W,
+                                                d2.BF16 if cfg.act_bf16 else d2.F32) > 0)
+    launches = cfg.layers * attn_k + cfg.sites + 2 + 2 + 2
+    tiny = torch.empty(1, device=dev)
+    node_floor_ms = timed(lambda r: tiny.fill_(float(r)), 64)
     sb = stage_bytes(cfg, n_acc_sets)
     stage_hbm = {"block_attn": {"bytes_per_call": a_bytes, "achieved": achieved,
                                 "frac": achieved / HBM_PEAK_GBS}}
@@ -452,6 +460,8 @@ def main():
         "step_event_ms": ev_ms / args.steps,
         "ms_per_step_host_sync": ms_sync,
         "mean_accepted": mean_acc,
+        "launch_chain": {"kernels_per_step": launches, "graph_node_floor_us": node_floor_ms * 1e3,
+                         "floor_us_per_step": launches * node_floor_ms * 1e3},
         "cpu_baseline": None,
         "lmhead_topk16": lmhead,
         "proj": proj,
