@@ -186,14 +186,15 @@ __global__ __launch_bounds__(kThreads) void verify_rows_kernel(
   // (the proposals and slots, and on an f32 target every slot's candidates and q)
   __shared__ int32_t allc[kMaxN * kTopK];
   __shared__ float allq[kMaxN * kTopK];
+  // (only row group 0 can need them: a sampled sequence uses no other group)
   int32_t x_pre = -1, sl_pre = -1;
-  if (t < N) {
+  if (grp == 0 && t < N) {
     x_pre = tokens[(int64_t)b * N + t];
     sl_pre = slot[(int64_t)b * N + t];
   }
   int32_t ci_pre = -1;
   float q_pre = 0.0f;
-  if (sizeof(typename KT::elem_t) == 4 && t < N * kTopK) {
+  if (sizeof(typename KT::elem_t) == 4 && grp == 0 && t < N * kTopK) {
     ci_pre = cidx[(int64_t)b * N * kTopK + t];
     q_pre = q[(int64_t)b * N * kTopK + t];
   }
