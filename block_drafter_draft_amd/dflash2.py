@@ -56,6 +56,7 @@ SIGNATURES = {
     "dflash2_verify": ([_vp, _i32, _i64, _i64, _i32] + [_vp] * 5 + [_u64, _u64, _i32, _i32] + [_vp] * 4 + [_sz, _vp], _i32),
     "dflash2_verify_workspace_bytes": ([_i32] * 4, _sz),
     "dflash2_ring_update": ([_vp] * 7 + [_i32] * 7 + [_vp, _vp], _i32),
+    "dflash2_eval_fn": ([_vp, _vp, _i64, _i32, _vp], _i32),
     "dflash2_status_string": ([_i32], ctypes.c_char_p),
     "dflash2_version": ([], _i32),
 }
@@ -250,6 +251,20 @@ def proj(hidden, B, N, row0, seq_stride, row_stride, weight, out=None, out_seq_s
                            _ptr(out), out_seq_stride, out_row_stride, _ptr(ws),
                            0 if ws is None else ws.numel(), _stream(stream))
     _check(rc, "dflash2_proj")
+    return out
+
+
+def eval_fn(x, which, out=None, stream=None):
+    """The library's exp_c (which 0, x <= 0) or log_c (which 1, x > 0), elementwise, on a
+    contiguous f32 tensor."""
+    _dev(x)
+    _contig(x)
+    if x.dtype != torch.float32:
+        raise TypeError("x must be float32")
+    if out is None:
+        out = torch.empty_like(x)
+    rc = _lib.dflash2_eval_fn(_ptr(x), _ptr(out), x.numel(), which, _stream(stream))
+    _check(rc, "dflash2_eval_fn")
     return out
 
 

@@ -324,6 +324,23 @@ int dflash2_verify(const void *target, int dtype, int64_t seq_stride, int64_t ro
 size_t dflash2_verify_workspace_bytes(int B, int N, int V, int dtype);
 
 /* A short English description of a return code or of one status bit. */
+/*
+ * dflash2_eval_fn - the library's fixed binary32 functions, evaluated elementwise, so that
+ * a caller can check them against its own implementation of the same steps. The sampled
+ * selector walk forms q with exp_c ("[Spec Decode] DFlash2: local convolution + candidate
+ * selector - #52816", PR description: inverse-CDF walk at T > 0 returning q for the
+ * lossless verify); the draft tree normalises with exp_c and log_c ("qwen35: DSpark
+ * speculative decoding (Qwen3.8-27B drafters) - #625", DDTree commit).
+ *   which = 0: out[i] = exp_c(x[i]) for x <= 0: 2^k P7(r) with a two-constant Cody-Waite
+ *              reduction and a degree-7 Taylor polynomial in Horner form with fma, every
+ *              step one correctly rounded binary32 operation; results under e^-87 are 0
+ *   which = 1: out[i] = log_c(x[i]) for finite x > 0: exponent split with the mantissa in
+ *              [sqrt(1/2), sqrt(2)), 2 atanh(u) by a degree-9 odd series, same rules
+ *   x, out: n f32 (out may not alias x). Inputs outside a function's domain give
+ *   unspecified values, not errors. No workspace.
+ */
+int dflash2_eval_fn(const float *x, float *out, int64_t n, int which, hipStream_t stream);
+
 const char *dflash2_status_string(int code);
 
 /* Library version as major*10000 + minor*100 + patch. */

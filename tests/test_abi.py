@@ -264,3 +264,12 @@ def test_proj_rejects():
     assert call(ws=NUL) == d2.EWORKSPACE
     assert d2.proj_workspace_bytes(2, 8, 640, 5120) > 0
     assert d2.proj_workspace_bytes(256, 8, 640, 5120) == 0  # enough output tiles already
+
+
+def test_eval_fn_rejects():
+    L = d2.lib()
+    assert L.dflash2_eval_fn(NUL, FAKE, 16, 0, None) == d2.EINVAL
+    assert L.dflash2_eval_fn(FAKE, NUL, 16, 0, None) == d2.EINVAL
+    assert L.dflash2_eval_fn(FAKE, FAKE, -1, 0, None) == d2.EINVAL
+    assert L.dflash2_eval_fn(FAKE, FAKE, 16, 2, None) == d2.EUNSUPPORTED
+    assert L.dflash2_eval_fn(FAKE, FAKE, 0, 1, None) == d2.OK          # nothing to launch
