@@ -1023,3 +1023,49 @@ def test_selector_gate_takes_slots_one_to_n(orc):
     for b in range(B):
         for i in range(1, P):
             np.testing.assert_array_equal(g[b, i - 1], (10 * b + i) * np.arange(1, R + 1))
+
+
+def _best_path_full_width(s1, s):
+    """Brute force over all K^N paths (N = 7, K = 16: 268,435,456 of them): every path's
+    score summed left to right in binary32 (the order the max-sum recursion adds in), the
+    three-slot prefixes enumerated in a loop and the four-slot suffixes vectorised. s[i] is
+    the transition from slot i + 1 to slot i + 2. Returns the best path, its score and the
+    runner-up score."""
+    K = s1.shape[0]
+    f = np.float32
+    a4, a5, a6, a7 = (a.ravel() for a in np.meshgrid(np.arange(K), np.arange(K), np.arange(K),
+                                                      np.arange(K), indexing="ij"))
+    t34 = s[2][:, a4]                                  # [K (k3), K^4]
+    t45, t56, t67 = s[3][a4, a5], s[4][a5, a6], s[5][a6, a7]
+    best, second, arg = -np.inf, -np.inf, None
+    for k1 in range(K):
+        for k2 in range(K):
+            p2 = f(f(s1[k1]) + f(s[0][k1, k2]))
+            for k3 in range(K):
+                t = (f(p2 + s[1][k2, k3]) + t34[k3]).astype(f)
+                t = (t + t45).astype(f)
+                t = (t + t56).astype(f)
+                t = (t + t67).astype(f)
+                i = int(np.argmax(t))
+                m = float(t[i])
+                if m > best:
+                    second = max(best, float(np.partition(t, -2)[-2]))
+                    best = m
+                    arg = (k1, k2, k3, int(a4[i]), int(a5[i]), int(a6[i]), int(a7[i]))
+                else:
+                    second = max(second, m)
+    return np.array(arg, dtype=np.int32), best, second
+
+
+@pytest.mark.parametrize("seed", [31, 32])
+def test_viterbi_exhaustive_full_width(orc, seed):
+    # the survey's full shape, N = 7 slots of K = 16 candidates: the recursion's path must
+    # be the path with the largest binary32 score among all 16^7 (real-valued scores, so
+    # the maximum is unique; the test checks that it is)
+    rng = np.random.default_rng(seed)
+    K, N = 16, 7
+    s1 = rng.normal(0, 2, K).astype(np.float32)
+    s = rng.normal(0, 2, (N - 1, K, K)).astype(np.float32)
+    want, best, second = _best_path_full_width(s1, s)
+    assert best > second, "the maximum is not unique for this seed"
+    np.testing.assert_array_equal(orc.viterbi(s1, s), want)
