@@ -157,7 +157,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the DFlash2 step shards by sequence with no "
-              "exchange, and this build has no multi-GPU path (--gpus must be 1)", file=sys.stderr)
+              "exchange, and no multi-GPU path is implemented (--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

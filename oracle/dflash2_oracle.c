@@ -99,7 +99,8 @@ void or_philox4x64_10(const uint64_t ctr_in[4], const uint64_t key_in[2], uint64
   out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
 }
 
-/* Draw layout (reading; the north star only fixes "keyed by seed, sequence, position"):
+/* Draw layout (a reading: the uniforms need only be tied to the seed, the sequence and the
+ * block position):
  * key = (seed, 0); counter = (step, b, j, 0). Word 0 is the selector-walk uniform for
  * slot j, word 1 the accept uniform for proposal j, word 2 the residual or bonus draw for
  * the token emitted at block position j; word 3 is unused. */
