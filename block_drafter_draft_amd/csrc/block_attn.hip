@@ -680,49 +680,115 @@ void launch_combine(const float* ws_o, const float2* ws_ml, int B, int P, int Hq
     launch_combine_w<D, 32>(ws_o, ws_ml, B, P, Hq, Hkv, nsplit, out, stream);
 }
 
-// f32: one wave per query row; lanes hold d and d + 64.
-__global__ __launch_bounds__(256) void attn_f32_kernel(
+// f32: keys in LDS tiles of 64; a lane scores one key per row, then accumulates columns.
+constexpr int kF32Waves = 16;                    // one workgroup per (sequence, KV head)
+constexpr int kF32RowsPerWave = 64 / kF32Waves;  // query rows per wave (at most 64 rows)
+
+template <int D>
+__global__ __launch_bounds__(64 * kF32Waves) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ kb, const float* __restrict__ vb,
     const float* __restrict__ kr, const float* __restrict__ vr, const int32_t* __restrict__ ctx_len,
-    int P, int Hq, int Hkv, int D, int S, int W, float scale, float* __restrict__ out) {
+    int P, int Hq, int Hkv, int S, int W, float scale, float* __restrict__ out) {
+  // binary32 path (small shapes: at most 64 query rows per KV head, D 64 or 128). The keys of
+  // one (sequence, KV head) are listed as slot 0's window (the widest) then the P block
+  // keys, and go through LDS in tiles of 64, each one coalesced round trip. Per tile, lane
+  // j of a wave scores key j against one query row, the wave takes the tile's maximum and
+  // sum by shuffles (online softmax), and lane d accumulates output columns d and d + 64
+  // over the tile's keys. A key outside a row's window gets weight 0. The dot products and
+  // the column sums each run four partial sums (fixed order), so the LDS reads pipeline.
+  constexpr int T = 64;
+  __shared__ float qs[64][D];
+  __shared__ float ks[T][D + 1];  // padded: lanes read 64 different rows of one column
+  __shared__ float vs[T][D];
+  __shared__ float ps[kF32Waves][T];
   const int g = blockIdx.x, b = blockIdx.y;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int G = Hq / Hkv, rows = P * G;
   int L = ctx_len[b];
   L = L < 0 ? 0 : L;
-  for (int n = w; n < rows; n += 4) {
-    const int slot = n / G, head = g * G + n % G;
-    const float* qr = q + (((int64_t)b * P + slot) * Hq + head) * D;
-    const float q0 = lane < D ? qr[lane] : 0.0f, q1 = lane + 64 < D ? qr[lane + 64] : 0.0f;
-    float m = -INFINITY, l = 0.0f, o0 = 0.0f, o1 = 0.0f;
-    int j0 = L + slot - W + 1;
-    j0 = j0 < 0 ? 0 : j0;
-    const int nkeys = (L - j0) + P;
-    for (int e = 0; e < nkeys; ++e) {
-      const float *kp, *vp;
-      if (e < L - j0) {
-        const int64_t r = (((int64_t)b * S + (j0 + e) % S) * Hkv + g) * D;
-        kp = kr + r;
-        vp = vr + r;
-      } else {
-        const int64_t r = (((int64_t)b * P + (e - (L - j0))) * Hkv + g) * D;
-        kp = kb + r;
-        vp = vb + r;
-      }
-      float part = (lane < D ? q0 * kp[lane] : 0.0f) + (lane + 64 < D ? q1 * kp[lane + 64] : 0.0f);
+  const int j0 = L - W + 1 > 0 ? L - W + 1 : 0;  // oldest context position of slot 0
+  const int nctx = L - j0, nkeys = nctx + P;
+  for (int e = t; e < rows * D; e += 64 * kF32Waves) {
+    const int n = e / D, d = e - n * D;
+    qs[n][d] = q[(((int64_t)b * P + n / G) * Hq + g * G + n % G) * D + d];
+  }
+  // per-row online-softmax state; wave w owns rows w, w + kF32Waves, ...
+  float m[kF32RowsPerWave], l[kF32RowsPerWave], o0[kF32RowsPerWave], o1[kF32RowsPerWave];
 #pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
-      const float sc = part * scale;
-      const float mn = fmaxf(m, sc);
-      const float a = expf(m - mn), p = expf(sc - mn);
-      l = l * a + p;
-      o0 = o0 * a + p * (lane < D ? vp[lane] : 0.0f);
-      o1 = o1 * a + p * (lane + 64 < D ? vp[lane + 64] : 0.0f);
-      m = mn;
+  for (int r = 0; r < kF32RowsPerWave; ++r) {
+    m[r] = -INFINITY;
+    l[r] = 0.0f;
+    o0[r] = 0.0f;
+    o1[r] = 0.0f;
+  }
+  for (int k0 = 0; k0 < nkeys; k0 += T) {
+    __syncthreads();  // the previous tile is no longer read (and qs is written)
+    for (int e = t; e < T * D; e += 64 * kF32Waves) {
+      const int j = e / D, d = e - j * D, kk = k0 + j;
+      float kv = 0.0f, vv = 0.0f;
+      if (kk < nkeys) {
+        const int64_t r = kk < nctx
+            ? (((int64_t)b * S + (j0 + kk) % S) * Hkv + g) * D
+            : (((int64_t)b * P + (kk - nctx)) * Hkv + g) * D;
+        kv = (kk < nctx ? kr : kb)[r + d];
+        vv = (kk < nctx ? vr : vb)[r + d];
+      }
+      ks[j][d] = kv;
+      vs[j][d] = vv;
     }
-    float* dst = out + (((int64_t)b * P + slot) * Hq + head) * D;
-    if (lane < D) dst[lane] = o0 / l;
-    if (lane + 64 < D) dst[lane + 64] = o1 / l;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kF32RowsPerWave; ++r) {
+      const int n = w + kF32Waves * r;
+      if (n >= rows) continue;  // uniform over the wave
+      const int slot = n / G;
+      const int kk = k0 + lane;
+      // context key kk (position j0 + kk) is in slot's window iff j0 + kk >= L + slot - W + 1
+      const bool vis = kk < nctx ? j0 + kk >= L + slot - W + 1 : kk < nkeys;
+      float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int d = 0; d < D; d += 4)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) s4[u] += qs[n][d + u] * ks[lane][d + u];
+      float sc = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+      sc = vis ? sc * scale : -INFINITY;
+      float tmax = sc;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o, 64));
+      const float mn = fmaxf(m[r], tmax);
+      const float base = mn == -INFINITY ? 0.0f : mn;
+      const float a = expf(m[r] - base);
+      const float pj = vis ? expf(sc - base) : 0.0f;
+      float psum = pj;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) psum += __shfl_xor(psum, o, 64);
+      ps[w][lane] = pj;
+      __builtin_amdgcn_wave_barrier();
+      float a0[4] = {0.0f, 0.0f, 0.0f, 0.0f}, a1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int j = 0; j < T; j += 4)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float pv = ps[w][j + u];
+          a0[u] += pv * vs[j + u][lane];
+          if constexpr (D > 64) a1[u] += pv * vs[j + u][lane + 64];
+        }
+      const float acc0 = (a0[0] + a0[1]) + (a0[2] + a0[3]);
+      const float acc1 = (a1[0] + a1[1]) + (a1[2] + a1[3]);
+      __builtin_amdgcn_wave_barrier();  // ps is rewritten for the next row
+      l[r] = l[r] * a + psum;
+      o0[r] = o0[r] * a + acc0;
+      o1[r] = o1[r] * a + acc1;
+      m[r] = mn;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kF32RowsPerWave; ++r) {
+    const int n = w + kF32Waves * r;
+    if (n >= rows) continue;
+    float* dst = out + (((int64_t)b * P + n / G) * Hq + g * G + n % G) * D;
+    dst[lane] = o0[r] / l[r];
+    if constexpr (D > 64) dst[lane + 64] = o1[r] / l[r];
   }
 }
 
@@ -813,9 +879,14 @@ extern "C" int dflash2_block_attn(const void* q, const void* k_blk, const void* 
   const int rows = P * (Hq / Hkv);
   if (dtype == DFLASH2_F32) {
     if (rows > 64) return DFLASH2_EUNSUPPORTED;
-    attn_f32_kernel<<<dim3(Hkv, B), 256, 0, stream>>>(
-        (const float*)q, (const float*)k_blk, (const float*)v_blk, (const float*)k_ring,
-        (const float*)v_ring, ctx_len, P, Hq, Hkv, D, S, W, scale, (float*)out);
+    if (D == 64)
+      attn_f32_kernel<64><<<dim3(Hkv, B), 64 * kF32Waves, 0, stream>>>(
+          (const float*)q, (const float*)k_blk, (const float*)v_blk, (const float*)k_ring,
+          (const float*)v_ring, ctx_len, P, Hq, Hkv, S, W, scale, (float*)out);
+    else
+      attn_f32_kernel<128><<<dim3(Hkv, B), 64 * kF32Waves, 0, stream>>>(
+          (const float*)q, (const float*)k_blk, (const float*)v_blk, (const float*)k_ring,
+          (const float*)v_ring, ctx_len, P, Hq, Hkv, S, W, scale, (float*)out);
     return launch_status();
   }
   if (dtype != DFLASH2_BF16) return DFLASH2_EUNSUPPORTED;

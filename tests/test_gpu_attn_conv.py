@@ -98,6 +98,10 @@ def test_attn_f32_shapes(d2):
     L = [0, 10, 100]
     q, kb, vb, kr, vr = _rand_attn(rng, 3, 8, 8, 1, 128, 96, bf16=False)
     run_attn(d2, q, kb, vb, kr, vr, L, 64, "f32 D128")
+    # several 64-key tiles (307 keys, ragged), two KV heads, ring wrap-around
+    rng = np.random.default_rng(53)
+    q, kb, vb, kr, vr = _rand_attn(rng, 2, 8, 8, 2, 64, 512, bf16=False)
+    run_attn(d2, q, kb, vb, kr, vr, [500, 900], 300, "f32 five tiles")
 
 
 def test_attn_scale_and_large_values(d2):
