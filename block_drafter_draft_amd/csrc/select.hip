@@ -242,7 +242,7 @@ __global__ __launch_bounds__(64) void select_path_kernel(
   __shared__ float S[kMaxN][kTopK][kTopK];
   __shared__ int32_t bp[kMaxN][kTopK];
   __shared__ float dp[kTopK];
-  __shared__ float e_sh[kTopK];
+  __shared__ float e_sh[2 * kTopK];
   __shared__ float uni[kMaxN];
   __shared__ int32_t path[kMaxN];
   __shared__ float qout[kMaxN][kTopK];
@@ -327,36 +327,69 @@ __global__ __launch_bounds__(64) void select_path_kernel(
   __syncthreads();
 
   if (mode == 0) {
-    // Viterbi: lane k holds the best prefix score ending at candidate k of the slot
+    // Viterbi. Lane (k = lane % 16, g = lane / 16) scores candidate k of the slot from the
+    // four predecessors 4g .. 4g + 3, in increasing order with a strict comparison, and two
+    // exchanges across g keep the larger score, the smaller predecessor on equal scores.
+    // That is the first maximum over the 16 predecessors in order, the sequential rule.
+    // The scores are finite, so their sums are never NaN.
+    const int k = lane & (kTopK - 1), g = lane >> 4;
     if (lane < kTopK) dp[lane] = S[0][0][lane];
     __syncthreads();
     for (int i = 2; i <= N; ++i) {
-      float best = 0.0f;
-      int arg = -1;
-      if (lane < kTopK) {
-        for (int kp = 0; kp < kTopK; ++kp) {
-          const float v = __fadd_rn(dp[kp], S[i - 1][kp][lane]);
-          if (arg < 0 || v > best) {
-            best = v;
-            arg = kp;
-          }
+      float d4[4], s4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        d4[j] = dp[4 * g + j];
+        s4[j] = S[i - 1][4 * g + j][k];
+      }
+      float best = __fadd_rn(d4[0], s4[0]);
+      int arg = 4 * g;
+#pragma unroll
+      for (int j = 1; j < 4; ++j) {
+        const float v = __fadd_rn(d4[j], s4[j]);
+        if (v > best) {
+          best = v;
+          arg = 4 * g + j;
         }
+      }
+#pragma unroll
+      for (int o = 16; o <= 32; o <<= 1) {
+        const float ob = __shfl_xor(best, o, 64);
+        const int oa = __shfl_xor(arg, o, 64);
+        if (ob > best || (ob == best && oa < arg)) {
+          best = ob;
+          arg = oa;
+        }
+      }
+      __syncthreads();  // every lane has read dp
+      if (lane < kTopK) {
         bp[i - 1][lane] = arg;
+        dp[lane] = best;
       }
       __syncthreads();
-      if (lane < kTopK) dp[lane] = best;
-      __syncthreads();
+    }
+    // the last slot's first maximum over the 16 candidates, the same way
+    float best = dp[k];
+    int last = k;
+#pragma unroll
+    for (int o = 1; o < kTopK; o <<= 1) {
+      const float ob = __shfl_xor(best, o, 64);
+      const int ol = __shfl_xor(last, o, 64);
+      if (ob > best || (ob == best && ol < last)) {
+        best = ob;
+        last = ol;
+      }
     }
     if (lane == 0) {
-      int last = 0;
-      for (int k = 1; k < kTopK; ++k)
-        if (dp[k] > dp[last]) last = k;
       path[N - 1] = last;
       for (int i = N; i >= 2; --i) path[i - 2] = bp[i - 1][path[i - 1]];
     }
     __syncthreads();
     for (int e = lane; e < N * kTopK; e += 64) qq[e] = (e % kTopK) == path[e / kTopK] ? 1.0f : 0.0f;
   } else {
+    // Inverse-CDF walk. Each slot's 16 weights go through LDS once; every lane then forms
+    // the running sums in k order (the same additions as the definition) and finds the
+    // pick itself, so the slot needs one barrier and no broadcast.
     if (lane < N) uni[lane] = uniform24(philox_draw(seed, step, (uint32_t)b, (uint32_t)(lane + 1)).w[0]);
     __syncthreads();
     int prev = 0;
@@ -367,28 +400,31 @@ __global__ __launch_bounds__(64) void select_path_kernel(
       float m = s;
       for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
       m = __shfl(m, 0, 64);
-      if (lane < kTopK) e_sh[lane] = exp_c(__fmul_rn(__fsub_rn(s, m), invT));
+      const float e = exp_c(__fmul_rn(__fsub_rn(s, m), invT));
+      if (lane < kTopK) e_sh[(i & 1) * kTopK + lane] = e;  // two buffers: no barrier before the write
       __syncthreads();
-      if (lane == 0) {
-        float Z = 0.0f, C[kTopK];
-        for (int k = 0; k < kTopK; ++k) {
-          Z = __fadd_rn(Z, e_sh[k]);
-          C[k] = Z;
-        }
-        const float tau = __fmul_rn(uni[i - 1], Z);
-        int pick = kTopK - 1;
-        for (int k = 0; k < kTopK; ++k)
-          if (C[k] > tau) {
-            pick = k;
-            break;
-          }
-        path[i - 1] = pick;
-        uni[i - 1] = Z;  // this slot's uniform is used; its place now carries Z
+      float ev[kTopK];
+#pragma unroll
+      for (int kk = 0; kk < kTopK; ++kk) ev[kk] = e_sh[(i & 1) * kTopK + kk];
+      const float u = uni[i - 1];
+      float Z = 0.0f;
+      int pick = -1;
+      float C[kTopK];
+#pragma unroll
+      for (int kk = 0; kk < kTopK; ++kk) {
+        Z = __fadd_rn(Z, ev[kk]);
+        C[kk] = Z;
       }
-      __syncthreads();
-      if (lane < kTopK) qout[i - 1][lane] = __fdiv_rn(e_sh[lane], uni[i - 1]);
-      prev = path[i - 1];
+      const float tau = __fmul_rn(u, Z);
+#pragma unroll
+      for (int kk = kTopK - 1; kk >= 0; --kk)
+        if (C[kk] > tau) pick = kk;
+      pick = pick < 0 ? kTopK - 1 : pick;
+      if (lane < kTopK) qout[i - 1][lane] = __fdiv_rn(e, Z);
+      if (lane == 0) path[i - 1] = pick;
+      prev = pick;
     }
+    __syncthreads();
     for (int e = lane; e < N * kTopK; e += 64) qq[e] = qout[e / kTopK][e % kTopK];
   }
   if (lane < N) {

@@ -140,3 +140,31 @@ def test_select_rejections_and_ties(d2):
     assert st[0] & orc.ST_NONFINITE and st[1] & orc.ST_NONFINITE
     assert st[2] & orc.ST_BADTOKEN and st[3] & orc.ST_BADTOKEN
     assert st[5] & orc.ST_BADTEMP and st[6] & orc.ST_BADTEMP
+
+
+def test_select_viterbi_ties_across_lane_groups(d2):
+    # With no transition term every predecessor of a candidate scores dp[kp] + val[k], so
+    # equal dp values tie; the path must take the first (smallest) predecessor and the first
+    # maximal last candidate. Ties are placed across the 4-predecessor groups the kernel
+    # reduces separately (3|4, 7|12, 0|15), and one sequence has integer values in {0, 1}.
+    rng = np.random.default_rng(45)
+    B, N, V, R = 6, 15, 700, 8
+    ci = np.stack([np.stack([rng.choice(V, 16, replace=False) for _ in range(N)])
+                   for _ in range(B)]).astype(np.int32)
+    cv = np.zeros((B, N, 16), np.float32)
+    cv[1] = rng.integers(0, 2, (N, 16))
+    cv[2, :, [3, 4]] = 1.0
+    cv[3, :, [7, 12]] = 2.0
+    cv[3, :, 9] = 1.0
+    cv[4, :, [0, 15]] = -1.0
+    cv[4, :, 1:15] = -2.0
+    cv[5] = rng.standard_normal((N, 16)).astype(np.float32)
+    g = np.zeros((B, N, R), np.float32)
+    g[5] = rng.standard_normal((N, R))
+    A = wl.to_bf16_bits(rng.normal(0, 0.25, (V, R)).astype(np.float32))
+    Bc = wl.to_bf16_bits(rng.normal(0, 0.25, (V, R)).astype(np.float32))
+    an = rng.integers(0, V, B).astype(np.int32)
+    tok, sl, q, st = run_both(d2, ci, cv, g, A, Bc, an, np.zeros(B, np.float32), 80, 1,
+                              what="viterbi ties")
+    assert not st.any()
+    assert np.all(sl[0] == 0) and np.all(sl[2] == 3) and np.all(sl[3] == 7) and np.all(sl[4] == 0)

@@ -291,3 +291,45 @@ def test_verify_greedy_special_rows(d2, f32):
                               1, 0, what=f"greedy special rows f32={f32} wrong={wrong}")
         if wrong is None:
             assert np.all(n == N)
+
+
+@pytest.mark.parametrize("sampled", [False, True])
+def test_verify_width_cap(d2, sampled):
+    # Verifying the first N_v of N = 7 proposals: the caller compacts the proposal arrays to
+    # N_v columns on the device; the target is read in place from the full 8-row block
+    # through its strides (rows 0..N_v). GPU and oracle must agree bit for bit.
+    rng = np.random.default_rng(41 + sampled)
+    B, N = 4, 7
+    if sampled:
+        V = 5003
+        logits = (rng.standard_normal((B, N + 1, V)) * 2).astype(np.float32)
+        target = np.stack([_softmax_rows(logits[b], 0.8) for b in range(B)])
+        temps = np.full(B, 0.8, np.float32)
+        tf = target
+    else:
+        cfg = wl.CONFIGS[2]
+        V = cfg.V
+        draft = wl.draft_logits(cfg)
+        one = wl.target_rows(cfg, draft)[0]                  # bf16 logits [8, V]
+        target = np.stack([np.roll(one, 977 * b, axis=1) for b in range(B)])
+        temps = np.zeros(B, np.float32)
+        tf = wl.bf16_bits_to_f32(target)
+    cand, q, slot, tok = make_proposals(rng, tf, N, V, accept_prefix=[7, 3, 1, 5])
+    tgt_dev = to_dev(np.ascontiguousarray(target).reshape(-1))
+    full = [to_dev(a) for a in (tok, cand, q, slot)]
+    for nv in (1, 3, 5):
+        say(f"verify width cap N_v={nv} of {N}, sampled={sampled}")
+        tok_c, cand_c, q_c, slot_c = (a[:, :nv].contiguous() for a in full)
+        st = torch.zeros(B, dtype=torch.int32, device=DEV)
+        n_acc = poison_like((B,), torch.int32)
+        out = poison_like((B, nv + 1), torch.int32)
+        d2.verify(tgt_dev, B, nv, (N + 1) * V, V, V, tok_c, cand_c, q_c, slot_c, to_dev(temps),
+                  11, nv, st, n_accept=n_acc, out_tokens=out)
+        torch.cuda.synchronize()
+        o = orc.verify(np.ascontiguousarray(target).reshape(-1), B, nv, (N + 1) * V, V, V,
+                       tok[:, :nv].copy(), cand[:, :nv].copy(), q[:, :nv].copy(),
+                       slot[:, :nv].copy(), temps, 11, nv)
+        for a, b_, name in zip((to_host(n_acc), to_host(out), to_host(st)), o,
+                               ("n_accept", "out_tokens", "status")):
+            np.testing.assert_array_equal(a, b_, err_msg=f"N_v={nv}: {name}")
+        assert np.all(to_host(n_acc) <= nv)

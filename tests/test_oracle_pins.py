@@ -623,6 +623,62 @@ def test_verify_greedy_chain_properties(orc):
     assert n_acc.max() == N
 
 
+def test_verify_width_cap(orc):
+    # Verifying only the first N_v < N proposals ("verify-width cap"): the same call with
+    # N = N_v over the first N_v proposals and target rows 0..N_v of the full block.
+    # Greedy, against the chain's definition written out: the accepted run is capped at N_v
+    # and the token after it is the first argmax of row min(n, N_v).
+    rng = np.random.default_rng(23)
+    B, N, V = 48, 7, 200
+    rows = rng.standard_normal((B, N + 1, V)).astype(np.float32)
+    am = rows.argmax(axis=2)
+    d = rng.integers(0, V, (B, N)).astype(np.int32)
+    for b in range(B):
+        d[b, :b % (N + 1)] = am[b, :b % (N + 1)]
+    z16 = np.zeros((B, N, 16), np.int32)
+    for nv in range(1, N):
+        n_acc, out, st = orc.verify(rows, B, nv, (N + 1) * V, V, V, d[:, :nv].copy(),
+                                    z16[:, :nv].copy(), z16[:, :nv].astype(np.float32),
+                                    np.zeros((B, nv), np.int32), np.zeros(B, np.float32), 0, 0)
+        assert not st.any() and out.shape == (B, nv + 1)
+        for b in range(B):
+            n = 0
+            while n < nv and d[b, n] == am[b, n]:
+                n += 1
+            assert n_acc[b] == n
+            np.testing.assert_array_equal(out[b, :n], d[b, :n])
+            assert out[b, n] == am[b, n] and np.all(out[b, n + 1:] == -1)
+    # Sampled: the uniforms are keyed by (step, sequence, row), so wherever the full-width
+    # call stops before N_v the capped call gives the same result; where every one of the
+    # N_v proposals is accepted, the token after them follows target row N_v.
+    V, N, M = 16, 4, 40_000
+    p = rng.dirichlet(np.ones(V)).astype(np.float32)
+    r = rng.dirichlet(np.ones(V) * 0.5).astype(np.float32)
+    for nv in (1, 2, 3):
+        target = np.stack([p] * nv + [r] + [p] * (N - nv)).astype(np.float32)
+        perm = rng.permutation(V).astype(np.int32)
+        ci = np.ascontiguousarray(np.broadcast_to(perm, (M, N, 16)))
+        qd = rng.dirichlet(np.ones(V)).astype(np.float32)
+        q = np.ascontiguousarray(np.broadcast_to(qd[perm], (M, N, 16)))
+        d = rng.choice(V, size=(M, N), p=qd / qd.sum()).astype(np.int32)
+        slot = np.argsort(perm)[d].astype(np.int32)
+        T = np.ones(M, np.float32)
+        fn, fo, fs = orc.verify(target, M, N, 0, V, V, d, ci, q, slot, T, 77, 3)
+        cn, co, cs = orc.verify(target, M, nv, 0, V, V, d[:, :nv].copy(), ci[:, :nv].copy(),
+                                q[:, :nv].copy(), slot[:, :nv].copy(), T, 77, 3)
+        assert not fs.any() and not cs.any()
+        early = fn < nv
+        np.testing.assert_array_equal(cn[early], fn[early])
+        for b in np.nonzero(early)[0][:2000]:
+            np.testing.assert_array_equal(co[b, :fn[b] + 1], fo[b, :fn[b] + 1])
+        full = ~early
+        assert np.all(cn[full] == nv)
+        np.testing.assert_array_equal(co[full, :nv], d[full, :nv])
+        k = int(full.sum())
+        assert k > 2000
+        assert _chi2(np.bincount(co[full, nv], minlength=V), r.astype(np.float64), k) < 37.70
+
+
 def test_verify_one_hot_target_sampled_equals_greedy(orc):
     rng = np.random.default_rng(18)
     B, N, V = 32, 7, 64
