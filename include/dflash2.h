@@ -57,7 +57,7 @@ extern "C" {
 /* return codes */
 #define DFLASH2_OK 0
 #define DFLASH2_EINVAL (-1)       /* null pointer, bad size or inconsistent shape */
-#define DFLASH2_EUNSUPPORTED (-2) /* a shape or type this build does not implement */
+#define DFLASH2_EUNSUPPORTED (-2) /* a shape or type the library does not implement */
 #define DFLASH2_EWORKSPACE (-3)   /* ws too small or misaligned */
 #define DFLASH2_EHIP (-4)         /* a kernel launch failed */
 

@@ -1115,7 +1115,7 @@ def _best_path_full_width(s1, s):
 
 @pytest.mark.parametrize("seed", [31, 32])
 def test_viterbi_exhaustive_full_width(orc, seed):
-    # the survey's full shape, N = 7 slots of K = 16 candidates: the recursion's path must
+    # the drafter's full shape, N = 7 slots of K = 16 candidates: the recursion's path must
     # be the path with the largest binary32 score among all 16^7 (real-valued scores, so
     # the maximum is unique; the test checks that it is)
     rng = np.random.default_rng(seed)
