@@ -235,7 +235,7 @@ def _special_greedy_rows(rng, V, f32):
         big = int(np.float32(50.0).view(np.uint32))
     else:
         pnan, nnan, pz, nz, pinf = 0x7FC1, 0xFFC0, 0x0000, 0x8000, 0x7F80
-        big = int(wl.to_bf16_bits(np.float32(50.0)))
+        big = int(wl.to_bf16_bits(np.float32(50.0))[0])
     for r in range(R):
         # sequence 0: NaN of either sign, sometimes both, at random depths
         pos = rng.choice(V, 3, replace=False)
