@@ -472,7 +472,7 @@ __global__ __launch_bounds__(64 * NW) void attn_stream_kernel(
       sc[i] = vis ? sc[i] * scale_log2 : -INFINITY;
       mx = fmaxf(mx, sc[i]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = fmaxf(mx, __uint_as_float(lane_xor32(__float_as_uint(mx), lane)));
     const float mnew = fmaxf(m, mx);
     const float base = mnew == -INFINITY ? 0.0f : mnew;
     const float alpha = exp2f(m - base);
@@ -482,7 +482,7 @@ __global__ __launch_bounds__(64 * NW) void attn_stream_kernel(
       sc[i] = exp2f(sc[i] - base);
       psum += sc[i];
     }
-    psum += __shfl_xor(psum, 32, 64);
+    psum += __uint_as_float(lane_xor32(__float_as_uint(psum), lane));
     l = l * alpha + psum;
     m = mnew;
     bf16x8_t pb[2];

@@ -212,6 +212,21 @@ __device__ __forceinline__ uint64_t quant40(float p) {
 // Wave helpers (wave64)
 // ---------------------------------------------------------------------------------------
 
+// The value held by lane l ^ 16 (or l ^ 32) of the wave, through the CDNA4 row swaps: with
+// both operands x, v_permlane16_swap leaves each odd row of the first result holding the
+// even row before it and each even row of the second result holding the odd row after it
+// (rows of 16 lanes); v_permlane32_swap does the same for the two halves of the wave.
+// VALU operations, so the exchange takes no LDS round trip. Only for code where all 64
+// lanes are active (the helpers below serve divergent code too and keep the permutes).
+__device__ __forceinline__ uint32_t lane_xor16(uint32_t x, int lane) {
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return (lane & 16) ? r[0] : r[1];
+}
+__device__ __forceinline__ uint32_t lane_xor32(uint32_t x, int lane) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return (lane & 32) ? r[0] : r[1];
+}
+
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   uint32_t lo = __shfl_xor((uint32_t)v, m, 64);
   uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, 64);

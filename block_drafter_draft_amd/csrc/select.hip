@@ -233,20 +233,6 @@ __global__ __launch_bounds__(256) void select_lattice_q8_kernel(
   lattice[(((int64_t)b * N + (i - 1)) * kTopK + kp) * kTopK + k] = __fadd_rn(cv, acc);
 }
 
-// The value held by lane l ^ 16 (or l ^ 32) of the wave, through the CDNA4 row swaps: with
-// both operands x, v_permlane16_swap leaves each odd row of the first result holding the
-// even row before it and each even row of the second result holding the odd row after it
-// (rows of 16 lanes); v_permlane32_swap does the same for the two halves of the wave.
-// VALU operations, so the exchange takes no LDS round trip. All 64 lanes must be active.
-__device__ __forceinline__ uint32_t lane_xor16(uint32_t x, int lane) {
-  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-  return (lane & 16) ? r[0] : r[1];
-}
-__device__ __forceinline__ uint32_t lane_xor32(uint32_t x, int lane) {
-  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-  return (lane & 32) ? r[0] : r[1];
-}
-
 __global__ __launch_bounds__(64) void select_path_kernel(
     const int32_t* __restrict__ cidx, const float* __restrict__ cval, int V,
     const int32_t* __restrict__ anchor, const float* __restrict__ temperature, uint64_t seed,
