@@ -227,6 +227,24 @@ __device__ __forceinline__ uint32_t lane_xor32(uint32_t x, int lane) {
   return (lane & 32) ? r[0] : r[1];
 }
 
+// DPP partners within a row of 16 lanes (CDNA DPP controls): the lane 8 and 4 places on
+// (rotating within the row), then the lane two and one away within its group of four. For a
+// reduction whose combining rule is associative and commutative (a maximum; a maximum with
+// ties to the smaller index), combining with these four partners in turn gives every lane
+// of the row the row's result, like the xor butterfly. All lanes of the row must be active.
+constexpr int kDppRowRor8 = 0x128, kDppRowRor4 = 0x124;
+constexpr int kDppQuadXor2 = 0x4E, kDppQuadXor1 = 0xB1;  // quad_perm [2,3,0,1], [1,0,3,2]
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_row(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, __uint_as_float(dpp_row<kDppRowRor8>(__float_as_uint(x))));
+  x = fmaxf(x, __uint_as_float(dpp_row<kDppRowRor4>(__float_as_uint(x))));
+  x = fmaxf(x, __uint_as_float(dpp_row<kDppQuadXor2>(__float_as_uint(x))));
+  return fmaxf(x, __uint_as_float(dpp_row<kDppQuadXor1>(__float_as_uint(x))));
+}
+
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   uint32_t lo = __shfl_xor((uint32_t)v, m, 64);
   uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, 64);

@@ -372,15 +372,20 @@ __global__ __launch_bounds__(64) void select_path_kernel(
     // the last slot's first maximum over the 16 candidates, the same way
     float best = dp[k];
     int last = k;
-#pragma unroll
-    for (int o = 1; o < kTopK; o <<= 1) {
-      const float ob = __shfl_xor(best, o, 64);
-      const int ol = __shfl_xor(last, o, 64);
+    auto take = [&](float ob, int ol) {
       if (ob > best || (ob == best && ol < last)) {
         best = ob;
         last = ol;
       }
-    }
+    };
+    take(__uint_as_float(dpp_row<kDppRowRor8>(__float_as_uint(best))),
+         (int)dpp_row<kDppRowRor8>((uint32_t)last));
+    take(__uint_as_float(dpp_row<kDppRowRor4>(__float_as_uint(best))),
+         (int)dpp_row<kDppRowRor4>((uint32_t)last));
+    take(__uint_as_float(dpp_row<kDppQuadXor2>(__float_as_uint(best))),
+         (int)dpp_row<kDppQuadXor2>((uint32_t)last));
+    take(__uint_as_float(dpp_row<kDppQuadXor1>(__float_as_uint(best))),
+         (int)dpp_row<kDppQuadXor1>((uint32_t)last));
     if (lane == 0) {
       path[N - 1] = last;
       for (int i = N; i >= 2; --i) path[i - 2] = bp[i - 1][path[i - 1]];
@@ -397,10 +402,8 @@ __global__ __launch_bounds__(64) void select_path_kernel(
     for (int i = 1; i <= N; ++i) {
       const int row = i == 1 ? 0 : prev;
       float s = lane < kTopK ? S[i - 1][row][lane] : -3.40282347e38f;
-      // the maximum is exact in any order
-      float m = s;
-      for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-      m = __shfl(m, 0, 64);
+      // the maximum is exact in any order: within lanes 0..15, then lane 0's to all
+      const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(row16_max(s)), 0));
       const float e = exp_c(__fmul_rn(__fsub_rn(s, m), invT));
       if (lane < kTopK) e_sh[(i & 1) * kTopK + lane] = e;  // two buffers: no barrier before the write
       __syncthreads();
