@@ -275,6 +275,38 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
+// Wave maxima for code where all 64 lanes are active: halves and rows are combined through
+// the row swaps, then each row through DPP. A maximum does not depend on the order in which
+// values are combined, so the result equals the butterfly's, in every lane.
+__device__ __forceinline__ uint32_t wave_max_u32_all(uint32_t v, int lane) {
+  uint32_t o = lane_xor32(v, lane);
+  v = o > v ? o : v;
+  o = lane_xor16(v, lane);
+  v = o > v ? o : v;
+  o = dpp_row<kDppRowRor8>(v);
+  v = o > v ? o : v;
+  o = dpp_row<kDppRowRor4>(v);
+  v = o > v ? o : v;
+  o = dpp_row<kDppQuadXor2>(v);
+  v = o > v ? o : v;
+  o = dpp_row<kDppQuadXor1>(v);
+  return o > v ? o : v;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64_all(uint64_t v, int lane) {
+  auto take = [&v](uint32_t lo, uint32_t hi) {
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    v = o > v ? o : v;
+  };
+  take(lane_xor32((uint32_t)v, lane), lane_xor32((uint32_t)(v >> 32), lane));
+  take(lane_xor16((uint32_t)v, lane), lane_xor16((uint32_t)(v >> 32), lane));
+  take(dpp_row<kDppRowRor8>((uint32_t)v), dpp_row<kDppRowRor8>((uint32_t)(v >> 32)));
+  take(dpp_row<kDppRowRor4>((uint32_t)v), dpp_row<kDppRowRor4>((uint32_t)(v >> 32)));
+  take(dpp_row<kDppQuadXor2>((uint32_t)v), dpp_row<kDppQuadXor2>((uint32_t)(v >> 32)));
+  take(dpp_row<kDppQuadXor1>((uint32_t)v), dpp_row<kDppQuadXor1>((uint32_t)(v >> 32)));
+  return v;
+}
+
 __device__ __forceinline__ int wave_or(int v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v |= __shfl_xor(v, m, 64);

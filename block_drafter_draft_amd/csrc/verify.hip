@@ -148,7 +148,7 @@ __device__ __forceinline__ uint64_t chunk_best_full(const uint32_t (&bits)[EPT],
   const bool special = mx > KT::kPosInf || mn < KT::kNegInf || mx == KT::kNegZeroRaw ||
                        mx == KT::kPosZero;
   if (__ballot(special)) return chunk_best_exact<KT, EPT, true>(bits, base, V);
-  const uint32_t M = wave_max_u32(mx);
+  const uint32_t M = wave_max_u32_all(mx, threadIdx.x & 63);  // every lane is active here
   const int wv = threadIdx.x >> 6;
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
@@ -416,7 +416,7 @@ __global__ __launch_bounds__(kThreads) void verify_finish_kernel(
         uint64_t m = pre[j][0];
         if (lane + 64 < nchunks) m = pre[j][1] > m ? pre[j][1] : m;
         if (lane >= nchunks) m = 0;
-        m = wave_max_u64(m);
+        m = wave_max_u64_all(m, lane);  // every lane is active here
         if (lane == 0 && r <= N) rowbest[r] = m;
       }
     } else {
