@@ -220,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void topk_wave_kernel(
         uint64_t m = 0;
 #pragma unroll
         for (int e = 0; e < EPT; ++e) m = pk[e] > m ? pk[e] : m;
-        const uint64_t g = wave_max_u64(m);
+        const uint64_t g = wave_max_u64_all(m, lane);  // the branch is wave-uniform
         if (lane == 0) list[cnt0 + k] = g;  // 0 (no candidate) ranks last
 #pragma unroll
         for (int e = 0; e < EPT; ++e)
