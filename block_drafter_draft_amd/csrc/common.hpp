@@ -293,6 +293,19 @@ __device__ __forceinline__ uint32_t wave_max_u32_all(uint32_t v, int lane) {
   return o > v ? o : v;
 }
 
+// Wave sum for code where all 64 lanes are active; integer addition is exact, so the
+// combining order does not matter.
+__device__ __forceinline__ uint64_t wave_sum_u64_all(uint64_t v, int lane) {
+  auto add = [&v](uint32_t lo, uint32_t hi) { v += ((uint64_t)hi << 32) | lo; };
+  add(lane_xor32((uint32_t)v, lane), lane_xor32((uint32_t)(v >> 32), lane));
+  add(lane_xor16((uint32_t)v, lane), lane_xor16((uint32_t)(v >> 32), lane));
+  add(dpp_row<kDppRowRor8>((uint32_t)v), dpp_row<kDppRowRor8>((uint32_t)(v >> 32)));
+  add(dpp_row<kDppRowRor4>((uint32_t)v), dpp_row<kDppRowRor4>((uint32_t)(v >> 32)));
+  add(dpp_row<kDppQuadXor2>((uint32_t)v), dpp_row<kDppQuadXor2>((uint32_t)(v >> 32)));
+  add(dpp_row<kDppQuadXor1>((uint32_t)v), dpp_row<kDppQuadXor1>((uint32_t)(v >> 32)));
+  return v;
+}
+
 __device__ __forceinline__ uint64_t wave_max_u64_all(uint64_t v, int lane) {
   auto take = [&v](uint32_t lo, uint32_t hi) {
     const uint64_t o = ((uint64_t)hi << 32) | lo;

@@ -291,8 +291,8 @@ __global__ __launch_bounds__(kThreads) void verify_rows_kernel(
     dz = (int64_t)quant40(d > 0.0f ? d : 0.0f) - (int64_t)quant40(p);
   }
   uint64_t zr = zp + (uint64_t)dz;
-  zp = wave_sum_u64(zp);
-  zr = wave_sum_u64(zr);
+  zp = wave_sum_u64_all(zp, t & 63);  // every lane is active here
+  zr = wave_sum_u64_all(zr, t & 63);
   fl = wave_or(fl);
   if ((t & 63) == 0) {
     red[t >> 6][0] = zr;
