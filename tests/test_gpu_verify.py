@@ -222,6 +222,59 @@ def test_verify_lossless_on_gpu(d2):
     assert chi2 < 37.70, chi2
 
 
+def test_verify_lossless_every_position_on_gpu(d2):
+    # N = 3 proposals, each slot with its own target row, candidate order and q; proposal j
+    # drawn from slot j's q. Every chunk of trials is bit-exact against the oracle, and over
+    # all 2^20 trials the token emitted at each block position k follows target row k among
+    # the trials that reach k (so a residual or an accept test that used another slot's
+    # candidates, q or row would fail).
+    rng = np.random.default_rng(40)
+    V, N = 16, 3
+    rows = rng.dirichlet(np.ones(V), N + 1).astype(np.float32)
+    qs = np.stack([0.5 * rows[j] + 0.5 * rng.dirichlet(np.ones(V)) for j in range(N)]).astype(np.float32)
+    perms = np.stack([rng.permutation(V) for _ in range(N)]).astype(np.int32)
+    qc = np.stack([qs[j][perms[j]] for j in range(N)]).astype(np.float32)
+    M, Bc = 1 << 20, (1 << 16) - 1
+    counts = np.zeros((N + 1, V), np.int64)
+    reached = np.zeros(N + 1, np.int64)
+    acc_hits = np.zeros(N, np.int64)
+    tgt_dev = to_dev(rows.reshape(-1))
+    done, step = 0, 0
+    while done < M:
+        B = min(Bc, M - done)
+        say(f"verify every-position chunk {step} B={B}")
+        d = np.stack([rng.choice(V, size=B, p=qs[j] / qs[j].sum()) for j in range(N)],
+                     axis=1).astype(np.int32)
+        slot = np.stack([np.argsort(perms[j])[d[:, j]] for j in range(N)], axis=1).astype(np.int32)
+        cand = np.ascontiguousarray(np.broadcast_to(perms, (B, N, 16)))
+        q = np.ascontiguousarray(np.broadcast_to(qc, (B, N, 16)))
+        T = np.ones(B, np.float32)
+        st = torch.zeros(B, dtype=torch.int32, device=DEV)
+        n_dev, out_dev, _ = d2.verify(tgt_dev, B, N, 0, V, V, to_dev(d), to_dev(cand), to_dev(q),
+                                      to_dev(slot), to_dev(T), 23, step, st)
+        n, out = to_host(n_dev), to_host(out_dev)
+        o = orc.verify(rows.reshape(-1), B, N, 0, V, V, d, cand, q, slot, T, 23, step)
+        np.testing.assert_array_equal(n, o[0], err_msg=f"chunk {step}: n_accept")
+        np.testing.assert_array_equal(out, o[1], err_msg=f"chunk {step}: out_tokens")
+        assert not to_host(st).any()
+        for k in range(N + 1):
+            r = n >= k
+            reached[k] += int(r.sum())
+            counts[k] += np.bincount(out[r, k], minlength=V)
+            if k < N:
+                acc_hits[k] += int((n[r] > k).sum())
+        done += B
+        step += 1
+    for k in range(N + 1):
+        e = reached[k] * rows[k].astype(np.float64)
+        chi2 = float(((counts[k] - e) ** 2 / e).sum())
+        assert chi2 < 37.70, (k, chi2)
+        if k < N:
+            want = np.minimum(rows[k].astype(np.float64), qs[k]).sum()
+            got = acc_hits[k] / reached[k]
+            assert abs(got - want) < 5 * np.sqrt(want * (1 - want) / reached[k]), (k, got, want)
+
+
 def _special_greedy_rows(rng, V, f32):
     """Six sequences of 8 rows whose maxima are decided by NaN, signed zeros, ties across
     lanes, waves, vectors and chunks, the ragged last chunk, and infinities."""

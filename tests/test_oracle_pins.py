@@ -545,6 +545,56 @@ def test_verify_lossless_chi_square(orc, seed):
     assert abs(n_acc.mean() - want) < 5 * np.sqrt(want * (1 - want) / M)
 
 
+def _slotwise_trials(orc, rows, perms, qs, M, seed, rng):
+    """M independent trials of one N-proposal block on a 16-token vocabulary. rows [N+1, V]
+    are the target rows (row j-1 verifies proposal j, row N gives the bonus); slot j has its
+    own candidate permutation perms[j] and its own draft distribution qs[j], and proposal j
+    is drawn from qs[j]. Every trial shares the rows through a zero sequence stride."""
+    N, V = qs.shape
+    cand = np.ascontiguousarray(np.broadcast_to(perms, (M, N, 16))).astype(np.int32)
+    qc = np.stack([qs[j][perms[j]] for j in range(N)]).astype(np.float32)
+    q = np.ascontiguousarray(np.broadcast_to(qc, (M, N, 16)))
+    d = np.stack([rng.choice(V, size=M, p=qs[j] / qs[j].sum()) for j in range(N)],
+                 axis=1).astype(np.int32)
+    slot = np.stack([np.argsort(perms[j])[d[:, j]] for j in range(N)], axis=1).astype(np.int32)
+    n_acc, out, st = orc.verify(rows.astype(np.float32), M, N, 0, V, V, d, cand, q, slot,
+                                np.ones(M, np.float32), seed, 0)
+    return n_acc, out, st, (d, cand, q, slot)
+
+
+@pytest.mark.parametrize("seed", [31, 32])
+def test_verify_lossless_at_every_position(orc, seed):
+    # "Geramy/LSE docs/DFLASH2.md", usage paragraph: the target checks every proposal of the
+    # block by probability-ratio rejection and samples the residual on the first rejection.
+    # Lossless means: for every block position k, the token the step emits there (the
+    # accepted proposal k+1, the residual draw, or the bonus) follows target row k, over the
+    # trials that reach position k (n_accept >= k). Each slot has its own target row, its own
+    # candidate order and its own q, so a residual or an accept test that takes another
+    # slot's candidates, q or row fails the chi-square at that position. The accept rate at
+    # slot j+1, among trials that reach it, is sum_x min(p_j, q_{j+1}).
+    rng = np.random.default_rng(seed)
+    V, N, M = 16, 3, 1_000_000
+    rows = rng.dirichlet(np.ones(V), N + 1)
+    # q of slot j+1 leans on row j so that later positions are reached often
+    qs = np.stack([0.5 * rows[j] + 0.5 * rng.dirichlet(np.ones(V)) for j in range(N)])
+    perms = np.stack([rng.permutation(V) for _ in range(N)]).astype(np.int32)
+    rows32 = rows.astype(np.float32)
+    qs32 = qs.astype(np.float32)
+    n_acc, out, st, _ = _slotwise_trials(orc, rows32, perms, qs32, M, seed, rng)
+    assert not st.any()
+    for k in range(N + 1):
+        reach = n_acc >= k
+        m = int(reach.sum())
+        assert m > 100_000, (k, m)
+        counts = np.bincount(out[reach, k], minlength=V)
+        chi2 = _chi2(counts, rows32[k].astype(np.float64), m)
+        assert chi2 < 37.70, (k, chi2)               # 15 dof, alpha = 1e-3
+        if k < N:
+            want = np.minimum(rows32[k].astype(np.float64), qs32[k]).sum()
+            got = float((n_acc[reach] > k).mean())
+            assert abs(got - want) < 5 * np.sqrt(want * (1 - want) / m), (k, got, want)
+
+
 def test_verify_special_cases(orc):
     rng = np.random.default_rng(16)
     V, M = 16, 50_000
