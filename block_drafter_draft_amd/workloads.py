@@ -125,6 +125,7 @@ _T_X, _T_BASE, _T_DELTA = 7, 8, 9
 _T_DRAFT, _T_TNOISE, _T_PRED, _T_SUCC, _T_GATE, _T_ANCHOR = 10, 11, 12, 13, 14, 15
 _T_HIDDEN, _T_HEAD = 16, 17
 _T_CONVPROJ, _T_GATEPROJ = 18, 19
+_T_BONUS, _T_ACCEPT = 20, 21
 
 
 def _rng(cfg: Config, tensor: int, *more: int) -> np.random.Generator:
@@ -197,14 +198,35 @@ def draft_logits(cfg: Config, seqs=None, iset: int = 0) -> np.ndarray:
     return _act(cfg, x)
 
 
+def bonus_draft_row(cfg: Config, seqs=None, iset: int = 0) -> np.ndarray:
+    """[B, 1, V] a draft-like row (same distribution, rounding and quantisation as the draft
+    logits) for the position after the block, which no draft row predicts: the base of the
+    target's bonus row."""
+    def gen(r, s):
+        x = _normal(r, s, cfg.draft_var)
+        if cfg.quantize_draft:
+            x = (np.round(x / cfg.quantize_draft) * cfg.quantize_draft).astype(np.float32)
+        return x
+    return _act(cfg, _per_seq(cfg, _T_BONUS, 0, seqs, iset, (1, cfg.V), gen))
+
+
 def target_rows(cfg: Config, draft: np.ndarray, seqs=None, iset: int = 0) -> np.ndarray:
-    """Target rows [B, P, V]: draft + noise as logits (same dtype as the draft), or as f32
-    probabilities softmax(logits / T) (T = 1 for greedy sequences)."""
+    """Target rows [B, P, V]: the draft row that predicts the same position plus noise, as
+    logits (same dtype as the draft), or as f32 probabilities softmax(logits / T) (T = 1 for
+    greedy sequences).
+
+    Alignment: target row r verifies proposal r + 1, which the selector takes from the
+    candidates of draft row r + 1, so target row r is built around draft row r + 1 (both
+    score the token at block position r + 1). Row P - 1, the bonus row, predicts the position
+    after the block; no draft row does, so its base is a draft-like row of its own stream."""
     seqs_l = list(range(cfg.B)) if seqs is None else list(seqs)
     d = bf16_bits_to_f32(draft) if draft.dtype == np.uint16 else draft
+    bonus = bonus_draft_row(cfg, seqs_l, iset)
+    bonus = bf16_bits_to_f32(bonus) if bonus.dtype == np.uint16 else bonus
+    base = np.concatenate([d[:, 1:], bonus], axis=1).astype(np.float32)
     noise = _per_seq(cfg, _T_TNOISE, 0, seqs_l, iset, (cfg.P, cfg.V),
                      lambda r, s: _normal(r, s, cfg.target_noise_var))
-    logits = d.astype(np.float32) + noise
+    logits = base + noise
     if cfg.target_kind == "logits":
         return _act(cfg, logits)
     temps = cfg.temperatures()[seqs_l]
@@ -315,27 +337,91 @@ class StepInputs:
 
 
 def make_step_inputs(cfg: Config, iset: int = 0, with_attention: bool = True,
-                     with_codebooks: bool = True, cb=None) -> StepInputs:
-    si = StepInputs(cfg=cfg, ctx_len=ctx_len(cfg, iset))
+                     with_codebooks: bool = True, cb=None, seqs=None) -> StepInputs:
+    """All inputs of one step. `seqs` (a list of sequence indices) draws only those
+    sequences, with exactly the values they have in the full batch."""
+    sel = slice(None) if seqs is None else list(seqs)
+    si = StepInputs(cfg=cfg, ctx_len=ctx_len(cfg, iset)[sel])
     if with_attention:
         for layer in range(cfg.layers):
-            si.q.append(attn_q(cfg, layer, iset=iset))
-            kb, vb = attn_block_kv(cfg, layer, iset=iset)
+            si.q.append(attn_q(cfg, layer, seqs, iset=iset))
+            kb, vb = attn_block_kv(cfg, layer, seqs, iset=iset)
             si.k_blk.append(kb)
             si.v_blk.append(vb)
-            kr, vr = attn_ring(cfg, layer, iset=iset)
+            kr, vr = attn_ring(cfg, layer, seqs, iset=iset)
             si.k_ring.append(kr)
             si.v_ring.append(vr)
     for site in range(cfg.sites):
-        x, base, delta = conv_inputs(cfg, site, iset=iset)
+        x, base, delta = conv_inputs(cfg, site, seqs, iset=iset)
         si.conv_x.append(x)
         si.conv_base.append(base)
         si.conv_delta.append(delta)
-    si.draft = draft_logits(cfg, iset=iset)
-    si.target = target_rows(cfg, si.draft, iset=iset)
+    si.draft = draft_logits(cfg, seqs, iset=iset)
+    si.target = target_rows(cfg, si.draft, seqs, iset=iset)
     if with_codebooks:
         si.pred_cb, si.succ_cb = cb if cb is not None else codebooks(cfg)
-    si.gate = gate(cfg, iset=iset)
-    si.anchor = anchor(cfg, iset)
-    si.temperature = cfg.temperatures()
+    si.gate = gate(cfg, seqs, iset=iset)
+    si.anchor = anchor(cfg, iset)[sel]
+    si.temperature = cfg.temperatures()[sel]
     return si
+
+
+@dataclass
+class VerifyInputs:
+    """Inputs of one verify call (bf16 as uint16 bit patterns)."""
+    target: np.ndarray        # [B, P, V]
+    tokens: np.ndarray        # [B, N]
+    cand_idx: np.ndarray      # [B, N, 16]
+    q: np.ndarray             # [B, N, 16]
+    slot: np.ndarray          # [B, N]
+    temperature: np.ndarray   # [B]
+
+
+def all_accept_verify_inputs(cfg: Config, iset: int = 0, seqs=None) -> VerifyInputs:
+    """Verify inputs under which every proposal of every sequence is accepted: the other
+    extreme from the step's own targets, for the verify call alone.
+
+    Per sequence and slot j: 16 distinct candidates, q ~ Dirichlet(1) over them, and the
+    proposal drawn from q. The target rows are the workload's own (target_rows), changed
+    only at each proposal: for a greedy sequence, row j-1 gets a strict maximum at d_j
+    (logits: 2 |max| + 1; probabilities: the row scaled by 1/2 plus 1/2 at d_j); for a
+    sampled sequence, row j-1 is scaled by 1 - q_j(d_j) and gets q_j(d_j) added at d_j, so
+    that p_t(d_j) >= q_j(d_j) (the ratio test then always accepts). Row N is unchanged."""
+    seqs_l = list(range(cfg.B)) if seqs is None else list(seqs)
+    N, V = cfg.N, cfg.V
+    draft = draft_logits(cfg, seqs_l, iset)
+    target = target_rows(cfg, draft, seqs_l, iset)
+    temps = cfg.temperatures()[seqs_l]
+    B = len(seqs_l)
+    cand = np.empty((B, N, 16), np.int32)
+    q = np.empty((B, N, 16), np.float32)
+    slot = np.empty((B, N), np.int32)
+    for n, b in enumerate(seqs_l):
+        r = _rng(cfg, _T_ACCEPT, 0, b, iset)
+        for j in range(N):
+            cand[n, j] = r.choice(V, 16, replace=False)
+            q[n, j] = r.dirichlet(np.ones(16)).astype(np.float32)
+            w = q[n, j].astype(np.float64)
+            slot[n, j] = r.choice(16, p=w / w.sum())
+    tokens = np.take_along_axis(cand, slot[..., None], axis=2)[..., 0].astype(np.int32)
+    for n in range(B):
+        for j in range(N):
+            d = tokens[n, j]
+            if target.dtype == np.uint16:           # bf16 logits: greedy
+                row = bf16_bits_to_f32(target[n, j])
+                top = float(np.max(np.abs(row)))
+                target[n, j, d] = to_bf16_bits(np.array([2 * top + 1], np.float32))[0]
+            elif temps[n] > 0:                      # probabilities, sampled
+                qd = np.float32(q[n, j, slot[n, j]])
+                row = target[n, j] * (np.float32(1) - qd)
+                row[d] += qd
+                target[n, j] = row
+            elif cfg.target_kind == "probs":        # probabilities, greedy
+                row = target[n, j] * np.float32(0.5)
+                row[d] += np.float32(0.5)
+                target[n, j] = row
+            else:                                   # f32 logits: greedy
+                top = float(np.max(np.abs(target[n, j])))
+                target[n, j, d] = np.float32(2 * top + 1)
+    return VerifyInputs(target=target, tokens=tokens, cand_idx=cand, q=q, slot=slot,
+                        temperature=temps)

@@ -323,7 +323,6 @@ int dflash2_verify(const void *target, int dtype, int64_t seq_stride, int64_t ro
                    void *ws, size_t ws_bytes, hipStream_t stream);
 size_t dflash2_verify_workspace_bytes(int B, int N, int V, int dtype);
 
-/* A short English description of a return code or of one status bit. */
 /*
  * dflash2_eval_fn - the library's fixed binary32 functions, evaluated elementwise, so that
  * a caller can check them against its own implementation of the same steps. The sampled
@@ -341,6 +340,7 @@ size_t dflash2_verify_workspace_bytes(int B, int N, int V, int dtype);
  */
 int dflash2_eval_fn(const float *x, float *out, int64_t n, int which, hipStream_t stream);
 
+/* A short English description of a return code or of one status bit. */
 const char *dflash2_status_string(int code);
 
 /* Library version as major*10000 + minor*100 + patch. */

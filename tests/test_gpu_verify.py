@@ -386,3 +386,19 @@ def test_verify_width_cap(d2, sampled):
                                ("n_accept", "out_tokens", "status")):
             np.testing.assert_array_equal(a, b_, err_msg=f"N_v={nv}: {name}")
         assert np.all(to_host(n_acc) <= nv)
+
+
+@pytest.mark.parametrize("c", [2, 5])
+def test_verify_all_accept_inputs(d2, c):
+    # the workload's targets changed only at the proposals so that every proposal is
+    # accepted: greedy sequences then read every row, sampled ones draw the bonus
+    cfg = wl.CONFIGS[c]
+    seqs = list(range(min(cfg.B, 12)))
+    vi = wl.all_accept_verify_inputs(cfg, iset=0, seqs=seqs)
+    B = len(seqs)
+    for step in (0, 1):
+        n, out, st = run_both(d2, vi.target, vi.target.dtype == np.uint16, B, cfg.N,
+                              cfg.P * cfg.V, cfg.V, cfg.V, vi.tokens, vi.cand_idx, vi.q,
+                              vi.slot, vi.temperature, cfg.seed, step,
+                              what=f"all-accept config {c} step {step}")
+        assert np.all(n == cfg.N) and not st.any()
