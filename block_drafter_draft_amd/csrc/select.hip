@@ -11,6 +11,8 @@
 // Kernel 2 (one wave per sequence): the nonfinite/index checks, then the max-sum path
 // (Viterbi, ties to the lower slot) when greedy, or the inverse-CDF walk with exp_c and
 // Philox uniforms when sampled.
+#include <mutex>
+
 #include "common.hpp"
 
 namespace df2 {
@@ -615,20 +617,16 @@ extern "C" size_t dflash2_select_workspace_bytes(int B, int N) {
   return round_up((size_t)B * N * kTopK * kTopK * sizeof(float), kWsAlign);
 }
 
-extern "C" int dflash2_select(const int32_t* cand_idx, const float* cand_val, const float* gate,
-                              const uint16_t* pred_cb, const uint16_t* succ_cb, int V, int R,
-                              const int32_t* anchor, const float* temperature, uint64_t seed,
-                              uint64_t step, int B, int N, int32_t* tokens, int32_t* slot,
-                              float* q, int32_t* status, void* ws, size_t ws_bytes,
-                              hipStream_t stream) {
-  if (!cand_idx || !cand_val || !gate || !pred_cb || !succ_cb || !anchor || !temperature ||
-      !tokens || !slot || !q || !status || !ws)
-    return DFLASH2_EINVAL;
-  if (B < 1 || N < 1 || R < 1 || V < kTopK) return DFLASH2_EINVAL;
-  if (N > kMaxN || R > kMaxR || B > 65535) return DFLASH2_EUNSUPPORTED;
-  if (!aligned(ws, kWsAlign) || ws_bytes < dflash2_select_workspace_bytes(B, N))
-    return DFLASH2_EWORKSPACE;
-  float* lattice = (float*)ws;
+namespace df2 {
+namespace {
+
+// Both selector entry points: the host checks are done, `lattice` holds at least
+// dflash2_select_workspace_bytes(B, N) bytes of device memory.
+int select_launch(const int32_t* cand_idx, const float* cand_val, const float* gate,
+                  const uint16_t* pred_cb, const uint16_t* succ_cb, int V, int R,
+                  const int32_t* anchor, const float* temperature, uint64_t seed, uint64_t step,
+                  int B, int N, int32_t* tokens, int32_t* slot, float* q, int32_t* status,
+                  float* lattice, hipStream_t stream) {
   const int RS = lat_row_stride(R);
   // predecessor and successor rows (bf16), the gate, and the products fl(A g) (f32)
   const size_t lds = (size_t)2 * kTopK * RS * sizeof(uint16_t) + (size_t)RS * sizeof(float) +
@@ -646,6 +644,81 @@ extern "C" int dflash2_select(const int32_t* cand_idx, const float* cand_val, co
   select_path_kernel<<<B, 64, 0, stream>>>(cand_idx, cand_val, V, anchor, temperature, seed, step,
                                            N, lattice, tokens, slot, q, status);
   return launch_status();
+}
+
+int select_check(const int32_t* cand_idx, const float* cand_val, const float* gate,
+                 const uint16_t* pred_cb, const uint16_t* succ_cb, int V, int R,
+                 const int32_t* anchor, const float* temperature, int B, int N,
+                 const int32_t* tokens, const int32_t* slot, const float* q,
+                 const int32_t* status) {
+  if (!cand_idx || !cand_val || !gate || !pred_cb || !succ_cb || !anchor || !temperature ||
+      !tokens || !slot || !q || !status)
+    return DFLASH2_EINVAL;
+  if (B < 1 || N < 1 || R < 1 || V < kTopK) return DFLASH2_EINVAL;
+  if (N > kMaxN || R > kMaxR || B > 65535) return DFLASH2_EUNSUPPORTED;
+  return DFLASH2_OK;
+}
+
+// The allocation-free selector's lattice: a file-scope device array, one copy per GPU the
+// library runs on, held until the process ends. Host code never passes `scratch` itself
+// (on the host that name is not a device address); it passes the address that
+// hipGetSymbolAddress returns for the current device, looked up once per device.
+constexpr size_t kSelectScratchBytes = (size_t)4 << 20;
+__device__ __align__(256) unsigned char scratch[kSelectScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Address of this device's `scratch`, or nullptr on a HIP error.
+void* scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+}  // namespace df2
+
+extern "C" int dflash2_select(const int32_t* cand_idx, const float* cand_val, const float* gate,
+                              const uint16_t* pred_cb, const uint16_t* succ_cb, int V, int R,
+                              const int32_t* anchor, const float* temperature, uint64_t seed,
+                              uint64_t step, int B, int N, int32_t* tokens, int32_t* slot,
+                              float* q, int32_t* status, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  const int rc = select_check(cand_idx, cand_val, gate, pred_cb, succ_cb, V, R, anchor,
+                              temperature, B, N, tokens, slot, q, status);
+  if (rc != DFLASH2_OK) return rc;
+  if (!ws) return DFLASH2_EINVAL;
+  if (!aligned(ws, kWsAlign) || ws_bytes < dflash2_select_workspace_bytes(B, N))
+    return DFLASH2_EWORKSPACE;
+  return select_launch(cand_idx, cand_val, gate, pred_cb, succ_cb, V, R, anchor, temperature,
+                       seed, step, B, N, tokens, slot, q, status, (float*)ws, stream);
+}
+
+extern "C" size_t dflash2_select_noalloc_max_bytes(void) { return kSelectScratchBytes; }
+
+extern "C" int dflash2_select_noalloc(const int32_t* cand_idx, const float* cand_val,
+                                      const float* gate, const uint16_t* pred_cb,
+                                      const uint16_t* succ_cb, int V, int R,
+                                      const int32_t* anchor, const float* temperature,
+                                      uint64_t seed, uint64_t step, int B, int N,
+                                      int32_t* tokens, int32_t* slot, float* q, int32_t* status,
+                                      hipStream_t stream) {
+  const int rc = select_check(cand_idx, cand_val, gate, pred_cb, succ_cb, V, R, anchor,
+                              temperature, B, N, tokens, slot, q, status);
+  if (rc != DFLASH2_OK) return rc;
+  if (dflash2_select_workspace_bytes(B, N) > kSelectScratchBytes) return DFLASH2_EWORKSPACE;
+  void* lattice = scratch_for_current_device();
+  if (!lattice) return DFLASH2_EHIP;
+  return select_launch(cand_idx, cand_val, gate, pred_cb, succ_cb, V, R, anchor, temperature,
+                       seed, step, B, N, tokens, slot, q, status, (float*)lattice, stream);
 }
 
 extern "C" int dflash2_select_q8(const int32_t* cand_idx, const float* cand_val,

@@ -50,6 +50,8 @@ SIGNATURES = {
     "dflash2_proj_workspace_bytes": ([_i32] * 4, _sz),
     "dflash2_select": ([_vp] * 5 + [_i32, _i32, _vp, _vp, _u64, _u64, _i32, _i32] + [_vp] * 5 + [_sz, _vp], _i32),
     "dflash2_select_workspace_bytes": ([_i32] * 2, _sz),
+    "dflash2_select_noalloc": ([_vp] * 5 + [_i32, _i32, _vp, _vp, _u64, _u64, _i32, _i32] + [_vp] * 5, _i32),
+    "dflash2_select_noalloc_max_bytes": ([], _sz),
     "dflash2_ddtree": ([_vp] * 5 + [_i32, _i32, _vp, _i32, _i32, _i32] + [_vp] * 7 + [_sz, _vp], _i32),
     "dflash2_ddtree_workspace_bytes": ([_i32] * 2, _sz),
     "dflash2_select_q8": ([_vp] * 9 + [_i32, _i32, _vp, _vp, _u64, _u64, _i32, _i32] + [_vp] * 5 + [_sz, _vp], _i32),
@@ -293,6 +295,30 @@ def select(cand_idx, cand_val, gate, pred_cb, succ_cb, anchor, temperature, seed
                              _ptr(tokens), _ptr(slot), _ptr(q), _ptr(status), _ptr(ws),
                              ws.numel(), _stream(stream))
     _check(rc, "dflash2_select")
+    return tokens, slot, q, status
+
+
+def select_noalloc_max_bytes() -> int:
+    return int(_lib.dflash2_select_noalloc_max_bytes())
+
+
+def select_noalloc(cand_idx, cand_val, gate, pred_cb, succ_cb, anchor, temperature, seed, step,
+                   tokens, slot, q, status, stream=None):
+    """dflash2_select without a workspace (the library's static lattice); every output is
+    caller-provided so that the call allocates nothing."""
+    _dev(cand_idx, cand_val, gate, pred_cb, succ_cb, anchor, temperature, tokens, slot, q, status)
+    _contig(cand_idx, cand_val, gate, pred_cb, succ_cb, anchor, temperature, tokens, slot, q,
+            status)
+    B, N, _ = cand_idx.shape
+    V, R = pred_cb.shape
+    if pred_cb.dtype != torch.bfloat16 or succ_cb.dtype != torch.bfloat16:
+        raise TypeError("codebooks must be bfloat16")
+    rc = _lib.dflash2_select_noalloc(_ptr(cand_idx), _ptr(cand_val), _ptr(gate), _ptr(pred_cb),
+                                     _ptr(succ_cb), V, R, _ptr(anchor), _ptr(temperature),
+                                     int(seed) & (2**64 - 1), int(step) & (2**64 - 1), B, N,
+                                     _ptr(tokens), _ptr(slot), _ptr(q), _ptr(status),
+                                     _stream(stream))
+    _check(rc, "dflash2_select_noalloc")
     return tokens, slot, q, status
 
 

@@ -245,6 +245,27 @@ int dflash2_select(const int32_t *cand_idx, const float *cand_val, const float *
 size_t dflash2_select_workspace_bytes(int B, int N);
 
 /*
+ * dflash2_select_noalloc - dflash2_select for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments without the workspace, the same kernels and the same results. The
+ * lattice lives in a static device array of dflash2_select_noalloc_max_bytes() bytes (4 MiB),
+ * one copy per GPU, held until the process ends; its address is looked up once per device,
+ * with that device current, on the device's first call (thread-safe). The call allocates
+ * nothing and never synchronises. The stream must belong to the current device.
+ * Requires dflash2_select_workspace_bytes(B, N) <= dflash2_select_noalloc_max_bytes()
+ * (B * N <= 4096 lattice rows of 16 x 16 binary32 scores), else DFLASH2_EWORKSPACE; a failed
+ * address lookup returns DFLASH2_EHIP. Every call on one GPU shares that GPU's array: calls
+ * that overlap in time on one GPU (other streams, other threads) race and must not be made.
+ * The lattice is fully written before it is read, so nothing needs clearing between calls.
+ */
+int dflash2_select_noalloc(const int32_t *cand_idx, const float *cand_val, const float *gate,
+                           const uint16_t *pred_cb, const uint16_t *succ_cb, int V, int R,
+                           const int32_t *anchor, const float *temperature, uint64_t seed,
+                           uint64_t step, int B, int N, int32_t *tokens, int32_t *slot, float *q,
+                           int32_t *status, hipStream_t stream);
+size_t dflash2_select_noalloc_max_bytes(void);
+
+/*
  * dflash2_ddtree - a draft tree by best-first expansion over the selector lattice ("qwen35:
  * DSpark speculative decoding (Qwen3.8-27B drafters) - #625", the DDTree commit: candidates
  * scored as draft log-probability plus the selector's compatibility with the branch's actual

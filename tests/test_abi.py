@@ -273,3 +273,16 @@ def test_eval_fn_rejects():
     assert L.dflash2_eval_fn(FAKE, FAKE, -1, 0, None) == d2.EINVAL
     assert L.dflash2_eval_fn(FAKE, FAKE, 16, 2, None) == d2.EUNSUPPORTED
     assert L.dflash2_eval_fn(FAKE, FAKE, 0, 1, None) == d2.OK          # nothing to launch
+
+
+def test_select_noalloc_rejects():
+    L = d2.lib()
+    p = ctypes.c_void_p(16)
+    cap = L.dflash2_select_noalloc_max_bytes()
+    assert cap == 4 << 20
+    args = lambda B, N, first=p: [first] + [p] * 4 + [1000, 16, p, p, 0, 0, B, N] + [p] * 4 + [None]
+    assert L.dflash2_select_noalloc(*args(1, 7, None)) == d2.EINVAL
+    assert L.dflash2_select_noalloc(*args(0, 7)) == d2.EINVAL
+    assert L.dflash2_select_noalloc(*args(1, 16)) == d2.EUNSUPPORTED
+    over = cap // (7 * 16 * 16 * 4) + 1                   # one sequence past the static lattice
+    assert L.dflash2_select_noalloc(*args(over, 7)) == d2.EWORKSPACE
