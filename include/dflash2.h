@@ -23,7 +23,8 @@
  *   - Every array pointer is DEVICE memory owned by the caller, and must stay valid until
  *     the work enqueued on `stream` has completed. The library allocates nothing, keeps no
  *     mutable global state (calls are thread-safe), never synchronises and never falls
- *     back to the host.
+ *     back to the host. The one exception is dflash2_select_noalloc, whose lattice is a
+ *     static device array per GPU (its per-device address is cached under a lock).
  *   - Calls enqueue kernels on `stream` (0 = the null stream) and return at once. The
  *     return value reports argument errors known on the host (DFLASH2_E*); nothing is
  *     launched when it is nonzero. Data-dependent problems are reported per sequence in
