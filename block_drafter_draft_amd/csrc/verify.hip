@@ -3,16 +3,27 @@
 // proposals, greedy keeps the deterministic chain; drafter-geometry paragraph: the target
 // consumes the anchor plus all proposals, so an all-accept step has a bonus row).
 //
-// Kernel 1 (grid: chunks x row groups x sequences) reads each needed target row chunk once:
-//   greedy  - rows 0..N: the chunk's first element under the top-16 order (packed word),
-//             a group of rows per workgroup;
+// Kernel 1 (grid: chunks x sequences) reads one row chunk per workgroup:
+//   greedy  - row 0: the chunk's first element under the top-16 order (packed word). The
+//             greedy chain needs row j only after proposals 1..j have all been accepted, so
+//             rows 1..N wait for kernel 2;
 //   sampled - the accept chain is cheap (N gathers and N Philox draws, one per lane), so
 //             every workgroup of the sequence recomputes it and then reads only the row it
 //             will draw from: the chunk sums of the integer weights floor(w * 2^40), both
 //             for p_t itself and with the 16 candidates' residual max(0, p_t - q) swapped in.
-// Kernel 2 (one workgroup per sequence) runs the greedy chain on the row maxima, or picks
-// the chunk holding the draw from the chunk sums and scans that one chunk in index order.
-// Integer weights make the draw independent of the summation order, so it is bit-exact.
+// Kernel 2 (grid: G workgroups per sequence):
+//   greedy  - every workgroup reduces row 0's chunk maxima and checks proposal 1. Rejected:
+//             workgroup 0 writes the result. Accepted: the G workgroups stream rows 1..N over
+//             their share of the chunks and fold each row's best into one word per row with
+//             an agent-scope atomic maximum; the last workgroup to arrive (an agent-scope
+//             counter) runs the chain on those words. The words and the counter travel only
+//             through agent-scope atomics, which are coherent across the XCDs' L2 caches
+//             without a release fence (a fence would write back the whole L2).
+//   sampled - workgroup 0 picks the chunk holding the draw from the chunk sums and scans
+//             that one chunk in index order. Integer weights make the draw independent of
+//             the summation order, so it is bit-exact.
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace df2 {
@@ -20,6 +31,11 @@ namespace {
 
 constexpr int kThreads = kChunkThreads;
 constexpr int kMaxN = 15;
+constexpr int kRowWords = 16;    // per-sequence atomic row words (rows 1..N; N <= 15)
+#ifndef DF2_VERIFY_RPP
+#define DF2_VERIFY_RPP 4
+#endif
+constexpr int kRowsPerPass = DF2_VERIFY_RPP;  // rows whose chunk loads are in flight together in kernel 2
 
 struct ChainRec {
   int32_t n_acc;   // accepted proposals
@@ -30,12 +46,14 @@ struct ChainRec {
 
 struct Ws {
   ChainRec* chain;   // [B]
-  uint64_t* best;    // [B][N+1][nchunks] greedy chunk maxima
+  uint64_t* best0;   // [B][nchunks] greedy row-0 chunk maxima
+  uint64_t* rowmax;  // [B][kRowWords] greedy row maxima of rows 1..N (agent-scope atomics)
+  uint32_t* arrive;  // [B] kernel-2 arrivals of an accepted greedy sequence (agent scope)
   uint64_t* zsum;    // [B][nchunks][2] sampled chunk sums (residual, plain)
   int32_t* zflag;    // [B][nchunks] status bits seen in the chunk
 };
 
-__host__ __device__ inline size_t ws_layout(int B, int N, int nchunks, Ws* w, char* base) {
+__host__ __device__ inline size_t ws_layout(int B, int nchunks, Ws* w, char* base) {
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -43,25 +61,43 @@ __host__ __device__ inline size_t ws_layout(int B, int N, int nchunks, Ws* w, ch
     return o;
   };
   size_t o_chain = take(sizeof(ChainRec) * B);
-  size_t o_best = take(sizeof(uint64_t) * (size_t)B * (N + 1) * nchunks);
+  size_t o_best = take(sizeof(uint64_t) * (size_t)B * nchunks);
+  size_t o_row = take(sizeof(uint64_t) * (size_t)B * kRowWords);
+  size_t o_arr = take(sizeof(uint32_t) * (size_t)B);
   size_t o_z = take(sizeof(uint64_t) * 2 * (size_t)B * nchunks);
   size_t o_f = take(sizeof(int32_t) * (size_t)B * nchunks);
   if (w && base) {
     w->chain = (ChainRec*)(base + o_chain);
-    w->best = (uint64_t*)(base + o_best);
+    w->best0 = (uint64_t*)(base + o_best);
+    w->rowmax = (uint64_t*)(base + o_row);
+    w->arrive = (uint32_t*)(base + o_arr);
     w->zsum = (uint64_t*)(base + o_z);
     w->zflag = (int32_t*)(base + o_f);
   }
   return off;
 }
 
-template <class KT>
-__device__ __forceinline__ uint32_t load_bits(const typename KT::elem_t* p, int64_t i) {
-  if constexpr (sizeof(typename KT::elem_t) == 2)
-    return reinterpret_cast<const uint16_t*>(p)[i];
-  else
-    return __float_as_uint(reinterpret_cast<const float*>(p)[i]);
+// Agent-scope (whole-GPU) relaxed atomics. Read-modify-write atomics are performed
+// coherently for all XCDs; loads and stores at this scope bypass the non-coherent parts of
+// the cache hierarchy (sc1). wait_vm makes a thread's earlier memory operations complete
+// (performed) before anything after it is issued, and keeps the compiler from moving memory
+// operations across it.
+__device__ __forceinline__ void store_agent(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void store_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t load_agent(uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void max_agent(uint64_t* p, uint64_t v) {
+  __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t add_agent(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_vm() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Accept chain of a sampled sequence, computed by wave 0 (lane j-1 tests proposal j) and
 // published in *rec (LDS). All threads must call; returns after a barrier.
@@ -166,9 +202,10 @@ __device__ __forceinline__ uint64_t chunk_best_full(const uint32_t (&bits)[EPT],
   return 0ull;  // not reached: some lane holds M
 }
 
-// Grid: (chunks, row groups, sequences). A greedy sequence's workgroup takes RG rows of
-// one chunk; a sampled sequence uses row group 0 only.
-template <class KT, int EPT, bool VEC, int RG>
+// Grid: (chunks, sequences). A greedy sequence's workgroup reduces its chunk of row 0; a
+// sampled sequence's workgroup recomputes the accept chain and sums its chunk of the row the
+// draw comes from.
+template <class KT, int EPT, bool VEC>
 __global__ __launch_bounds__(kThreads) void verify_rows_kernel(
     const typename KT::elem_t* __restrict__ target, int64_t seq_stride, int64_t row_stride, int V,
     const int32_t* __restrict__ tokens, const int32_t* __restrict__ cidx,
@@ -176,25 +213,24 @@ __global__ __launch_bounds__(kThreads) void verify_rows_kernel(
     const float* __restrict__ temperature, uint64_t seed, uint64_t step, int N, int nchunks,
     Ws ws) {
   constexpr int CH = EPT * kThreads;
-  const int chunk = blockIdx.x, grp = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  const int chunk = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const int base = chunk * CH;
   __shared__ ChainRec rec;
-  __shared__ uint64_t red[kThreads / 64][RG < 2 ? 2 : RG];  // the sampled path uses two
+  __shared__ uint64_t red[kThreads / 64][2];
   __shared__ int redf[kThreads / 64];
 
   // a sampled chain's first loads do not depend on the temperature: issue them with it
   // (the proposals and slots, and on an f32 target every slot's candidates and q)
   __shared__ int32_t allc[kMaxN * kTopK];
   __shared__ float allq[kMaxN * kTopK];
-  // (only row group 0 can need them: a sampled sequence uses no other group)
   int32_t x_pre = -1, sl_pre = -1;
-  if (grp == 0 && t < N) {
+  if (t < N) {
     x_pre = tokens[(int64_t)b * N + t];
     sl_pre = slot[(int64_t)b * N + t];
   }
   int32_t ci_pre = -1;
   float q_pre = 0.0f;
-  if (sizeof(typename KT::elem_t) == 4 && grp == 0 && t < N * kTopK) {
+  if (sizeof(typename KT::elem_t) == 4 && t < N * kTopK) {
     ci_pre = cidx[(int64_t)b * N * kTopK + t];
     q_pre = q[(int64_t)b * N * kTopK + t];
   }
@@ -206,42 +242,28 @@ __global__ __launch_bounds__(kThreads) void verify_rows_kernel(
   const typename KT::elem_t* tb = target + (int64_t)b * seq_stride;
 
   if (mode == 0) {
-    // greedy: the chunk's first element of rows r0 .. r0 + RG - 1, all loads issued together
-    const int r0 = grp * RG;
-    if (r0 > N) return;
-    uint32_t bits[RG][EPT];
+    // kernel 2's row words and arrival counter for this sequence start at zero
+    if (chunk == 0 && t < kRowWords) {
+      store_agent(ws.rowmax + (int64_t)b * kRowWords + t, 0ull);
+      if (t == 0) store_agent(ws.arrive + b, 0u);
+    }
+    uint32_t bits[EPT];
     const bool full = VEC && base + CH <= V;
-    // rows past N re-read row N (ignored below), so the loads carry no conditions
-    if (full) {
-#pragma unroll
-      for (int rr = 0; rr < RG; ++rr) {
-        const int r = r0 + rr <= N ? r0 + rr : N;
-        load_chunk_full<KT, EPT>(tb + (int64_t)r * row_stride, base, bits[rr]);
-      }
-    } else {
-#pragma unroll
-      for (int rr = 0; rr < RG; ++rr) {
-        const int r = r0 + rr <= N ? r0 + rr : N;
-        load_chunk<KT, EPT, VEC>(tb + (int64_t)r * row_stride, base, V, bits[rr]);
-      }
-    }
-#pragma unroll
-    for (int rr = 0; rr < RG; ++rr) {
-      uint64_t m = 0;
-      if (r0 + rr <= N)
-        m = full ? chunk_best_full<KT, EPT>(bits[rr], base, V)
-                 : chunk_best_exact<KT, EPT, VEC>(bits[rr], base, V);
-      if ((t & 63) == 0) red[t >> 6][rr] = m;
-    }
+    if (full)
+      load_chunk_full<KT, EPT>(tb, base, bits);
+    else
+      load_chunk<KT, EPT, VEC>(tb, base, V, bits);
+    const uint64_t m = full ? chunk_best_full<KT, EPT>(bits, base, V)
+                            : chunk_best_exact<KT, EPT, VEC>(bits, base, V);
+    if ((t & 63) == 0) red[t >> 6][0] = m;
     __syncthreads();
-    if (t < RG && r0 + t <= N) {
-      uint64_t g = red[0][t];
-      for (int w = 1; w < kThreads / 64; ++w) g = red[w][t] > g ? red[w][t] : g;
-      ws.best[((int64_t)b * (N + 1) + r0 + t) * nchunks + chunk] = g;
+    if (t == 0) {
+      uint64_t g = red[0][0];
+      for (int w = 1; w < kThreads / 64; ++w) g = red[w][0] > g ? red[w][0] : g;
+      ws.best0[(int64_t)b * nchunks + chunk] = g;
     }
     return;
   }
-  if (grp != 0) return;
 
   // sampled: which row, and with which candidate corrections
   const float* tgt = reinterpret_cast<const float*>(tb);
@@ -331,16 +353,33 @@ __device__ __forceinline__ uint64_t block_incl_scan_u64(uint64_t v, uint64_t* ws
   return v + add;
 }
 
-template <class KT, int EPT>
-__global__ __launch_bounds__(kThreads) void verify_finish_kernel(
+// Grid: B * G workgroups (see below); see the head of this file.
+#ifndef DF2_VERIFY_WPE
+#define DF2_VERIFY_WPE 0
+#endif
+template <class KT, int EPT, bool VEC>
+__global__
+#if DF2_VERIFY_WPE > 0
+__launch_bounds__(kThreads, DF2_VERIFY_WPE)
+#else
+__launch_bounds__(kThreads)
+#endif
+void verify_finish_kernel(
     const typename KT::elem_t* __restrict__ target, int64_t seq_stride, int64_t row_stride, int V,
     const int32_t* __restrict__ tokens, const int32_t* __restrict__ cidx,
     const float* __restrict__ q, const float* __restrict__ temperature, uint64_t seed,
-    uint64_t step, int N, int nchunks, Ws ws, int32_t* __restrict__ n_accept,
+    uint64_t step, int N, int nchunks, int G, Ws ws, int32_t* __restrict__ n_accept,
     int32_t* __restrict__ out_tokens, int32_t* __restrict__ status) {
   constexpr int CH = EPT * kThreads;
-  const int b = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
-  __shared__ uint64_t rowbest[kMaxN + 1];
+  // A 1-D grid of B * G workgroups. The first B are workgroup 0 of each sequence (the one
+  // that writes a rejected or sampled sequence's result), dispatched before any other; the
+  // rest go chunk-fastest, so that consecutive workgroups (which the hardware deals to
+  // different XCDs) share a sequence.
+  const int B = gridDim.x / G, L = blockIdx.x;
+  const int Gm = G > 1 ? G - 1 : 1;  // (with G = 1 every workgroup is a first one)
+  const int b = L < B ? L : (L - B) / Gm;
+  const int g = L < B ? 0 : 1 + (L - B) % Gm;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   __shared__ uint64_t wsum[kThreads / 64], wsum2[kThreads / 64];
   __shared__ uint64_t sh_z[2];
   __shared__ int sh_f[kThreads / 64];
@@ -351,31 +390,30 @@ __global__ __launch_bounds__(kThreads) void verify_finish_kernel(
   __shared__ float candq[kTopK];
   __shared__ int32_t allc[kMaxN * kTopK];
   __shared__ float allq[kMaxN * kTopK];
-
-  // The greedy chain's chunk maxima are loaded before the temperature is known (for up to
-  // 128 chunks: wave w takes rows w, w + 4, ..., lane l chunks l and l + 64), so that the
-  // two loads are one memory round trip; a sampled sequence ignores them.
-  constexpr int kRowIt = (kMaxN + 1 + kThreads / 64 - 1) / (kThreads / 64);
-  uint64_t pre[kRowIt][2];
   __shared__ int32_t dtok[kMaxN];
-  const int32_t my_tok = tokens[(int64_t)b * N + (t < N ? t : 0)];  // the proposals, with them
-  // the status word the selector left, read now so that the final update is a plain store
+  __shared__ uint64_t red[kThreads / 64][kRowsPerPass];
+  __shared__ uint64_t rowacc[kRowWords];
+  __shared__ uint64_t sh_row0;
+  __shared__ int sh_last;
+
+  // One memory round trip: the temperature, the proposals, the status word the selector
+  // left (so that the final update is a plain store), row 0's chunk maxima (wave 0, up to
+  // 128 chunks: lane l takes chunks l and l + 64), and for workgroup 0 of an f32 target a
+  // sampled sequence's chain record, this thread's chunk sums (chunks t*cpt .. t*cpt + cpt
+  // - 1, kept in registers for up to kCptMax chunks) and every slot's candidates. The
+  // workspace holds all of these for either target type; a sequence ignores what its
+  // mode does not use.
+  const float T = temperature[b];
+  const int32_t my_tok = tokens[(int64_t)b * N + (t < N ? t : 0)];
   const int32_t st_in = t == 0 ? status[b] : 0;
   const bool few = nchunks <= 128;
-  if (few) {
+  uint64_t pre0[2] = {0ull, 0ull};
+  if (few && w == 0) {
+    const uint64_t* src = ws.best0 + (int64_t)b * nchunks;
 #pragma unroll
-    for (int j = 0; j < kRowIt; ++j) {
-      const int r = min(w + (kThreads / 64) * j, N);
-      const uint64_t* src = ws.best + ((int64_t)b * (N + 1) + r) * nchunks;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) pre[j][i] = src[min(lane + 64 * i, nchunks - 1)];
-    }
+    for (int i = 0; i < 2; ++i) pre0[i] = src[min(lane + 64 * i, nchunks - 1)];
   }
   constexpr bool kIsF32 = sizeof(typename KT::elem_t) == 4;
-  // A sampled sequence's inputs do not depend on the temperature either: the chain record,
-  // this thread's chunk sums (chunks t*cpt .. t*cpt + cpt - 1, kept in registers for up to
-  // kCptMax chunks) and every slot's candidates, loaded in the same round trip. The
-  // workspace holds these arrays for either target type; a greedy sequence ignores them.
   constexpr int kCptMax = 4;
   const int cpt = (nchunks + kThreads - 1) / kThreads;
   ChainRec rec_pre = {0, 1, 0, 0};
@@ -384,22 +422,24 @@ __global__ __launch_bounds__(kThreads) void verify_finish_kernel(
   int32_t ci_pre = -1;
   float q_pre = 0.0f;
   if constexpr (kIsF32) {
-    rec_pre = ws.chain[b];
+    if (g == 0) {
+      rec_pre = ws.chain[b];
 #pragma unroll
-    for (int i = 0; i < kCptMax; ++i) {
-      const int c = min(t * cpt + i, nchunks - 1);
-      zr_pre[i] = ws.zsum[((int64_t)b * nchunks + c) * 2 + 0];
-      zp_pre[i] = ws.zsum[((int64_t)b * nchunks + c) * 2 + 1];
-      zf_pre[i] = ws.zflag[(int64_t)b * nchunks + c];
-    }
-    if (t < N * kTopK) {
-      ci_pre = cidx[(int64_t)b * N * kTopK + t];
-      q_pre = q[(int64_t)b * N * kTopK + t];
+      for (int i = 0; i < kCptMax; ++i) {
+        const int c = min(t * cpt + i, nchunks - 1);
+        zr_pre[i] = ws.zsum[((int64_t)b * nchunks + c) * 2 + 0];
+        zp_pre[i] = ws.zsum[((int64_t)b * nchunks + c) * 2 + 1];
+        zf_pre[i] = ws.zflag[(int64_t)b * nchunks + c];
+      }
+      if (t < N * kTopK) {
+        ci_pre = cidx[(int64_t)b * N * kTopK + t];
+        q_pre = q[(int64_t)b * N * kTopK + t];
+      }
     }
   }
   int st = 0;
   float invT = 0.0f;
-  int mode = temp_mode(temperature[b], &invT, &st);
+  int mode = temp_mode(T, &invT, &st);
   if (mode == 1 && !kIsF32) {
     st |= DFLASH2_ST_BADPROB;
     mode = 0;
@@ -409,32 +449,86 @@ __global__ __launch_bounds__(kThreads) void verify_finish_kernel(
   const typename KT::elem_t* tb = target + (int64_t)b * seq_stride;
 
   if (mode == 0) {
-    if (few) {
-#pragma unroll
-      for (int j = 0; j < kRowIt; ++j) {
-        const int r = w + (kThreads / 64) * j;
-        uint64_t m = pre[j][0];
-        if (lane + 64 < nchunks) m = pre[j][1] > m ? pre[j][1] : m;
-        if (lane >= nchunks) m = 0;
-        m = wave_max_u64_all(m, lane);  // every lane is active here
-        if (lane == 0 && r <= N) rowbest[r] = m;
-      }
-    } else {
-      for (int r = w; r <= N; r += kThreads / 64) {
-        uint64_t m = 0;
-        const uint64_t* src = ws.best + ((int64_t)b * (N + 1) + r) * nchunks;
+    // row 0's first element
+    if (w == 0) {
+      uint64_t m = 0;
+      if (few) {
+        m = lane < nchunks ? pre0[0] : 0ull;
+        if (lane + 64 < nchunks) m = pre0[1] > m ? pre0[1] : m;
+        m = wave_max_u64_all(m, lane);  // every lane of wave 0 is active here
+      } else {
+        const uint64_t* src = ws.best0 + (int64_t)b * nchunks;
         for (int c = lane; c < nchunks; c += 64) m = src[c] > m ? src[c] : m;
         m = wave_max_u64(m);
-        if (lane == 0) rowbest[r] = m;
       }
+      if (lane == 0) sh_row0 = m;
     }
     if (t < N) dtok[t] = my_tok;
+    if (t < kRowWords) rowacc[t] = 0ull;
+    __syncthreads();
+    const uint64_t r0 = sh_row0;
+    if (dtok[0] != (int32_t)cand_idx(r0)) {
+      // proposal 1 is rejected: the chain ends at row 0
+      if (g == 0 && t == 0) {
+        if (cand_key(r0) == KT::kNaN) st |= DFLASH2_ST_NONFINITE;
+        out[0] = (int32_t)cand_idx(r0);
+        for (int j = 1; j <= N; ++j) out[j] = -1;
+        n_accept[b] = 0;
+        status[b] = st_in | st;
+      }
+      return;
+    }
+    // Proposal 1 is accepted: this workgroup's chunks g, g + G, ... of rows 1..N, with
+    // the loads of up to kRowsPerPass rows in flight together (rows past N re-read row N,
+    // ignored, so that the loads carry no conditions).
+    for (int c = g; c < nchunks; c += G) {
+      const int base = c * CH;
+      const bool full = VEC && base + CH <= V;
+      for (int rp = 1; rp <= N; rp += kRowsPerPass) {
+        uint32_t bits[kRowsPerPass][EPT];
+        if (full) {
+#pragma unroll
+          for (int rr = 0; rr < kRowsPerPass; ++rr)
+            load_chunk_full<KT, EPT>(tb + (int64_t)min(rp + rr, N) * row_stride, base, bits[rr]);
+        } else {
+#pragma unroll
+          for (int rr = 0; rr < kRowsPerPass; ++rr)
+            load_chunk<KT, EPT, VEC>(tb + (int64_t)min(rp + rr, N) * row_stride, base, V,
+                                     bits[rr]);
+        }
+#pragma unroll
+        for (int rr = 0; rr < kRowsPerPass; ++rr) {
+          uint64_t m = 0;
+          if (rp + rr <= N)
+            m = full ? chunk_best_full<KT, EPT>(bits[rr], base, V)
+                     : chunk_best_exact<KT, EPT, VEC>(bits[rr], base, V);
+          if (lane == 0) red[w][rr] = m;
+        }
+        __syncthreads();
+        if (t < kRowsPerPass && rp + t <= N) {
+          uint64_t x = rowacc[rp + t];
+          for (int i = 0; i < kThreads / 64; ++i) x = red[i][t] > x ? red[i][t] : x;
+          rowacc[rp + t] = x;
+        }
+        __syncthreads();
+      }
+    }
+    // Publish: one atomic maximum per row, performed before this workgroup arrives.
+    if (t >= 1 && t <= N) max_agent(ws.rowmax + (int64_t)b * kRowWords + t, rowacc[t]);
+    wait_vm();
+    __syncthreads();
+    if (t == 0) sh_last = add_agent(ws.arrive + b, 1u) == (uint32_t)(G - 1);
+    __syncthreads();
+    if (!sh_last) return;
+    // The last workgroup: every other one's maxima were performed before its arrival.
+    if (t >= 1 && t <= N) rowacc[t] = load_agent(ws.rowmax + (int64_t)b * kRowWords + t);
     __syncthreads();
     if (t == 0) {
-      int n = 0;
+      int n = 1;  // proposal 1, checked above
       int32_t emitted = -1;
-      for (int j = 1; j <= N + 1; ++j) {
-        const uint64_t m = rowbest[j - 1];
+      if (cand_key(r0) == KT::kNaN) st |= DFLASH2_ST_NONFINITE;
+      for (int j = 2; j <= N + 1; ++j) {
+        const uint64_t m = rowacc[j - 1];
         const int32_t y = (int32_t)cand_idx(m);
         if (cand_key(m) == KT::kNaN) st |= DFLASH2_ST_NONFINITE;
         if (j <= N && dtok[j - 1] == y) {
@@ -450,6 +544,7 @@ __global__ __launch_bounds__(kThreads) void verify_finish_kernel(
     }
     return;
   }
+  if (g != 0) return;
 
   // sampled
   const ChainRec rec = rec_pre;
@@ -585,33 +680,29 @@ __global__ __launch_bounds__(kThreads) void verify_finish_kernel(
     float pv[EPT];
 #pragma unroll
     for (int e = 0; e < EPT; ++e) pv[e] = c0 + e < V ? row[c0 + e] : 0.0f;
-    int32_t ck[kTopK];
-    float qk[kTopK];
-#pragma unroll
-    for (int k = 0; k < kTopK; ++k) {
-      ck[k] = cand[k];
-      qk[k] = candq[k];
-    }
+    float pz[EPT];
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
-      const int x = c0 + e;
-      uint64_t r = 0;
-      if (x < V) {
-        const float p = prob_ok(pv[e], &dummy);
-        r = quant40(p);
-        // a candidate index replaces the weight by the residual; for a repeated index
-        // the first occurrence counts, so the candidates are applied last to first
+      pz[e] = c0 + e < V ? prob_ok(pv[e], &dummy) : 0.0f;
+      wgt[e] = c0 + e < V ? quant40(pz[e]) : 0ull;
+    }
+    // A candidate index replaces the weight by the residual; for a repeated index the first
+    // occurrence counts, so the candidates are applied last to first. They are read from LDS
+    // one at a time (every lane reads the same word), which keeps them out of registers.
 #pragma unroll
-        for (int k = kTopK - 1; k >= 0; --k) {
-          if (ck[k] == x) {
-            const float df = __fsub_rn(p, prob_ok(qk[k], &dummy));
-            r = quant40(df > 0.0f ? df : 0.0f);
-          }
+    for (int k = kTopK - 1; k >= 0; --k) {
+      const int32_t ck = cand[k];
+      const float qk = candq[k];
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        if (ck == c0 + e && c0 + e < V) {
+          const float df = __fsub_rn(pz[e], prob_ok(qk, &dummy));
+          wgt[e] = quant40(df > 0.0f ? df : 0.0f);
         }
       }
-      wgt[e] = r;
-      mine += r;
     }
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) mine += wgt[e];
     const uint64_t incl = block_incl_scan_u64(mine, wsum);
     const uint64_t excl = incl - mine;
     const uint64_t tau = sh_tau;
@@ -642,23 +733,25 @@ constexpr int kEPT = 8;  // elements per thread: one 16-byte bf16 vector or two 
 struct Plan {
   int nchunks;
   bool vec;
-  int rg;  // rows per greedy workgroup: 1, 2 or 4 (8 with DF2_VERIFY_RG)
+  int G;  // kernel-2 workgroups per sequence
 };
 
-// Rows per greedy workgroup: four (measured best at batch 16 and 64: fewer registers than
-// eight, so more workgroups in flight), fewer while the grid would have under about 1024
-// workgroups (batch 1 takes one row per workgroup).
-#ifndef DF2_VERIFY_RG
-#define DF2_VERIFY_RG 0  // 0: by the batch
+// Kernel 2 workgroups per sequence: one per chunk by default (0), so that even a single
+// accepted greedy chain streams rows 1..N over the whole chip in one or two round trips;
+// a positive value aims at that many workgroups in all instead. Measured at batch 64 (32
+// greedy sequences, 2 accepting proposal 1): one per chunk 32.0 us per call, about 4096 in
+// all 34.7, about 2048 in all 41.4, about 1024 in all 50.6 (the accepted chains then
+// stream their rows in eight latency-bound rounds).
+#ifndef DF2_VERIFY_FINISH_WGS
+#define DF2_VERIFY_FINISH_WGS 0
 #endif
-constexpr int kVerifyTargetWGs = 1024;
+constexpr int kFinishTargetWGs = DF2_VERIFY_FINISH_WGS;  // 0: one workgroup per chunk
 
-Plan make_plan(int B, int N, int V, int dtype, const void* target, int64_t ss, int64_t rs) {
+Plan make_plan(int B, int V, int dtype, const void* target, int64_t ss, int64_t rs) {
   Plan p;
   p.nchunks = (V + kEPT * kThreads - 1) / (kEPT * kThreads);
-  int rg = 4;
-  while (rg > 1 && (int64_t)B * p.nchunks * ((N + 1 + rg - 1) / rg) < kVerifyTargetWGs) rg >>= 1;
-  p.rg = DF2_VERIFY_RG ? DF2_VERIFY_RG : rg;
+  p.G = kFinishTargetWGs ? std::max(1, std::min(p.nchunks, kFinishTargetWGs / B)) : p.nchunks;
+  p.G = (int)std::min<int64_t>(p.G, INT32_MAX / B);  // the 1-D grid of B * G workgroups
   const int esz = dtype == DFLASH2_BF16 ? 2 : 4;
   p.vec = (target == nullptr || aligned(target, 16)) && (ss * esz) % 16 == 0 && (rs * esz) % 16 == 0;
   return p;
@@ -670,20 +763,11 @@ void launch(const Plan& p, const void* target, int64_t ss, int64_t rs, int V,
             const float* temp, uint64_t seed, uint64_t step, int B, int N, Ws w, int32_t* n_acc,
             int32_t* out, int32_t* status, hipStream_t st) {
   using E = typename KT::elem_t;
-  const dim3 grid(p.nchunks, (N + 1 + p.rg - 1) / p.rg, B);
-#define DF2_ROWS(RG)                                                                     \
-  verify_rows_kernel<KT, kEPT, VEC, RG><<<grid, kThreads, 0, st>>>(                      \
-      (const E*)target, ss, rs, V, tokens, cidx, q, slot, temp, seed, step, N, p.nchunks, w)
-  switch (p.rg) {
-    case 1: DF2_ROWS(1); break;
-    case 2: DF2_ROWS(2); break;
-    case 4: DF2_ROWS(4); break;
-    default: DF2_ROWS(8); break;
-  }
-#undef DF2_ROWS
-  verify_finish_kernel<KT, kEPT><<<B, kThreads, 0, st>>>((const E*)target, ss, rs, V, tokens, cidx,
-                                                         q, temp, seed, step, N, p.nchunks, w,
-                                                         n_acc, out, status);
+  verify_rows_kernel<KT, kEPT, VEC><<<dim3(p.nchunks, B), kThreads, 0, st>>>(
+      (const E*)target, ss, rs, V, tokens, cidx, q, slot, temp, seed, step, N, p.nchunks, w);
+  verify_finish_kernel<KT, kEPT, VEC><<<dim3(B * p.G), kThreads, 0, st>>>(
+      (const E*)target, ss, rs, V, tokens, cidx, q, temp, seed, step, N, p.nchunks, p.G, w, n_acc,
+      out, status);
 }
 
 template <class KT>
@@ -704,8 +788,8 @@ using namespace df2;
 
 extern "C" size_t dflash2_verify_workspace_bytes(int B, int N, int V, int dtype) {
   if (B < 1 || N < 1 || N > kMaxN || V < kTopK) return 0;
-  Plan p = make_plan(B, N, V, dtype, nullptr, 0, 0);
-  return ws_layout(B, N, p.nchunks, nullptr, nullptr);
+  Plan p = make_plan(B, V, dtype, nullptr, 0, 0);
+  return ws_layout(B, p.nchunks, nullptr, nullptr);
 }
 
 extern "C" int dflash2_verify(const void* target, int dtype, int64_t seq_stride, int64_t row_stride,
@@ -721,9 +805,9 @@ extern "C" int dflash2_verify(const void* target, int dtype, int64_t seq_stride,
   if (dtype != DFLASH2_BF16 && dtype != DFLASH2_F32) return DFLASH2_EUNSUPPORTED;
   if (!aligned(ws, kWsAlign) || ws_bytes < dflash2_verify_workspace_bytes(B, N, V, dtype))
     return DFLASH2_EWORKSPACE;
-  Plan p = make_plan(B, N, V, dtype, target, seq_stride, row_stride);
+  Plan p = make_plan(B, V, dtype, target, seq_stride, row_stride);
   Ws w;
-  ws_layout(B, N, p.nchunks, &w, (char*)ws);
+  ws_layout(B, p.nchunks, &w, (char*)ws);
   if (dtype == DFLASH2_BF16)
     launch_vec<KeyBF16>(p, target, seq_stride, row_stride, V, tokens, cand_idx, q, slot,
                         temperature, seed, step, B, N, w, n_accept, out_tokens, status, stream);

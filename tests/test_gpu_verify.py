@@ -402,3 +402,33 @@ def test_verify_all_accept_inputs(d2, c):
                               vi.slot, vi.temperature, cfg.seed, step,
                               what=f"all-accept config {c} step {step}")
         assert np.all(n == cfg.N) and not st.any()
+
+
+def test_verify_repeated_calls_share_one_workspace(d2):
+    # kernel 1 clears the accepted-chain row words and arrival counters that kernel 2 folds
+    # into with atomics; calls that reuse one workspace, each accepting different prefixes,
+    # must each match the oracle
+    rng = np.random.default_rng(41)
+    B, N, V = 48, 7, 30011
+    ws = d2.workspace(d2.verify_workspace_bytes(B, N, V, d2.F32), DEV)
+    ws.fill_(0xA5)                                          # stale contents, not zeros
+    for call in range(10):
+        logits = (rng.standard_normal((B, N + 1, V)) * 2).astype(np.float32)
+        temps = np.where(rng.random(B) < 0.5, 0.0, 0.8).astype(np.float32)
+        p_t = np.stack([_softmax_rows(logits[b], 0.8) for b in range(B)])
+        pref = rng.integers(0, N + 1, B)
+        cand, q, slot, tok = make_proposals(rng, p_t, N, V, accept_prefix=list(pref))
+        say(f"verify shared workspace call {call}")
+        st = torch.zeros(B, dtype=torch.int32, device=DEV)
+        n_dev = poison_like((B,), torch.int32)
+        o_dev = poison_like((B, N + 1), torch.int32)
+        d2.verify(to_dev(p_t.reshape(-1)), B, N, (N + 1) * V, V, V, to_dev(tok), to_dev(cand),
+                  to_dev(q), to_dev(slot), to_dev(temps), 13, call, st, n_accept=n_dev,
+                  out_tokens=o_dev, ws=ws)
+        torch.cuda.synchronize()
+        o = orc.verify(p_t.reshape(-1), B, N, (N + 1) * V, V, V, tok, cand, q, slot, temps, 13,
+                       call)
+        np.testing.assert_array_equal(to_host(n_dev), o[0], err_msg=f"call {call}: n_accept")
+        np.testing.assert_array_equal(to_host(o_dev), o[1], err_msg=f"call {call}: out_tokens")
+        np.testing.assert_array_equal(to_host(st), o[2], err_msg=f"call {call}: status")
+        assert (o[0][temps == 0] > 0).any()                 # some greedy chains go past row 0
