@@ -124,7 +124,10 @@ def host_info():
 
 def gpu_clocks():
     """Current sclk / mclk and the power cap as rocm-smi reports them (read before this
-    process touches the GPU; a child process, bounded in time)."""
+    process touches the GPU; a child process, bounded in time). Under a profiler, whose
+    preloaded library has initialised the GPU already, no child program is started."""
+    if any(k.startswith("ROCPROF") for k in os.environ) or "rocprof" in os.environ.get("LD_PRELOAD", ""):
+        return {"skipped": "running under a profiler"}
     try:
         r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--showmaxpower",
                             "--json"], capture_output=True, text=True, timeout=30)

@@ -329,6 +329,7 @@ constexpr int kTileKeys = 32;
 constexpr int kStreamD = 128;
 constexpr int kTileElems = kTileKeys * kStreamD;     // one tensor's tile (8 KiB of bf16)
 constexpr int kMergeStride = 40;                      // floats per d row of a merge state
+constexpr float kLazyLog2 = 8.0f;  // largest growth of a query's maximum before a rescale
 
 #define DF2_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
@@ -355,7 +356,8 @@ __global__ __launch_bounds__(64 * NW) void attn_stream_kernel(
   constexpr int D = kStreamD;
   __shared__ StreamSmem<NW> sm;
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int t = threadIdx.x, w = t >> 6, lane = t & 63, n = lane & 31, hh = lane >> 5;
+  const int t = threadIdx.x, lane = t & 63, n = lane & 31, hh = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform, so tile math is scalar
   const int G = Hq / Hkv, rows = P * G;
   int L = ctx_len[b];
   L = L < 0 ? 0 : L;
@@ -380,17 +382,42 @@ __global__ __launch_bounds__(64 * NW) void attn_stream_kernel(
     u32x4_t v = qvalid ? ld16(qrow + 16 * ks + 8 * hh) : u32x4_t{0, 0, 0, 0};
     qop[ks] = __builtin_bit_cast(bf16x8_t, v);
   }
-  // list index of this query's oldest visible context key (block keys are always visible)
+  // list index of this query's oldest visible context key (block keys are always visible),
+  // and the largest such index over all slots: a tile of context keys from there on is
+  // visible to every query
   const int kmin = L + slot_n - W + 1 - lo;
+  const int kmin_all = L + P - W - lo;
 
   // Copy of tile `tile` into buffer `buf`: instruction i moves rows 4i .. 4i+3; lane l
   // fetches chunk (l & 15) ^ swz(row) of row 4i + l / 16 into LDS slot l.
   const int64_t ring_b = (int64_t)b * S * Hkv * D + (int64_t)g * D;
   const int64_t blk_b = (int64_t)b * P * Hkv * D + (int64_t)g * D;
   const int lrow = lane >> 4;
+  // Context tiles that do not wrap around the ring (nearly all of them) take a cheap path:
+  // ring rows jm .. jm + 31 are consecutive, so lane l's row 4i + l/16 sits at a 32-bit byte
+  // offset (jm + l/16) * rowb + 4 i rowb from the sequence's ring base, plus its chunk, which
+  // depends on i only through i & 3.
+  const uint32_t rowb = (uint32_t)(Hkv * D * 2);
+  const char* kr_b = reinterpret_cast<const char*>(kr + ring_b);
+  const char* vr_b = reinterpret_cast<const char*>(vr + ring_b);
+  uint32_t coffb[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) coffb[k] = 16u * (uint32_t)(((lane & 15) ^ (lrow << 2)) ^ k);
   auto issue = [&](int tile, int buf) {
     const int kk0 = tile * kTileKeys;
     const int jm = kk0 < nctx ? (lo + kk0) % S : 0;  // ring row of list entry kk0 (if context)
+    uint16_t* dk = &sm.kv[w][buf][0][0];
+    uint16_t* dv = &sm.kv[w][buf][1][0];
+    if (kk0 + kTileKeys <= nctx && jm + kTileKeys <= S) {
+      const uint32_t rowbase = (uint32_t)(jm + lrow) * rowb;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t off = rowbase + (uint32_t)(4 * i) * rowb + coffb[i & 3];
+        __builtin_amdgcn_global_load_lds((const void*)(kr_b + off), DF2_LDS(dk + i * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vr_b + off), DF2_LDS(dv + i * 512), 16, 0, 0);
+      }
+      return;
+    }
     const uint16_t* ksrc[8];
     const uint16_t* vsrc[8];
 #pragma unroll
@@ -410,8 +437,6 @@ __global__ __launch_bounds__(64 * NW) void attn_stream_kernel(
       ksrc[i] = (ctx ? kr : kb) + (roff + coff);
       vsrc[i] = (ctx ? vr : vb) + (roff + coff);
     }
-    uint16_t* dk = &sm.kv[w][buf][0][0];
-    uint16_t* dv = &sm.kv[w][buf][1][0];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_global_load_lds((const void*)ksrc[i], DF2_LDS(dk + i * 512), 16, 0, 0);
@@ -464,27 +489,49 @@ __global__ __launch_bounds__(64 * NW) void attn_stream_kernel(
     }
     f32x16_t sc = s0 + s1;
     const int kk0 = tile * kTileKeys;
-    float mx = -INFINITY;
+    // A tile of context keys visible to every query (all but the window's first tile and
+    // the tiles holding block keys) needs no mask, and with a positive scale the scaling
+    // folds into the exponent's fma: max(scale s) = scale max(s). Otherwise the scores are
+    // masked and scaled first (sl = 1 then).
+    const bool fused = kk0 >= kmin_all && kk0 + kTileKeys <= nctx && scale_log2 > 0.0f;
+    float sl = scale_log2;
+    if (!fused) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kk = kk0 + 8 * (i >> 2) + 4 * hh + (i & 3);
-      const bool vis = kk < nctx ? kk >= kmin : kk < nkeys;
-      sc[i] = vis ? sc[i] * scale_log2 : -INFINITY;
-      mx = fmaxf(mx, sc[i]);
+      for (int i = 0; i < 16; ++i) {
+        const int kk = kk0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+        const bool vis = kk < nctx ? kk >= kmin : kk < nkeys;
+        sc[i] = vis ? sc[i] * scale_log2 : -INFINITY;
+      }
+      sl = 1.0f;
     }
+    float mx = sc[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
     mx = fmaxf(mx, __uint_as_float(lane_xor32(__float_as_uint(mx), lane)));
-    const float mnew = fmaxf(m, mx);
-    const float base = mnew == -INFINITY ? 0.0f : mnew;
-    const float alpha = exp2f(m - base);
+    const float mnew = fmaxf(m, mx * sl);
+    // Lazy rescale: the running maximum m is moved (and o, l rescaled) only when some
+    // query's maximum has grown by more than kLazyLog2 since; until then the stale m is
+    // the exponent base, so every weight stays below 2^kLazyLog2. The softmax is the same
+    // for any base; only the rounding of the intermediate sums differs.
+    if (__ballot(mnew > m + kLazyLog2) != 0) {
+      const float nb = mnew == -INFINITY ? 0.0f : mnew;
+      const float alpha = exp2f(m - nb);
+      if (!first) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+      }
+      l *= alpha;
+      m = mnew;
+    }
+    const float base = m == -INFINITY ? 0.0f : m;
     float psum = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      sc[i] = exp2f(sc[i] - base);
+      sc[i] = exp2f(fmaf(sc[i], sl, -base));
       psum += sc[i];
     }
     psum += __uint_as_float(lane_xor32(__float_as_uint(psum), lane));
-    l = l * alpha + psum;
-    m = mnew;
+    l += psum;
     bf16x8_t pb[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
@@ -497,7 +544,6 @@ __global__ __launch_bounds__(64 * NW) void attn_stream_kernel(
                    "+v"(vt[3][0][0]), "+v"(vt[3][0][1]), "+v"(vt[3][1][0]), "+v"(vt[3][1][1]));
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      if (!first) o[dt] *= alpha;  // on a wave's first tile o is still zero
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const u32x4_t w4 = {(uint32_t)vt[dt][u][0], (uint32_t)(vt[dt][u][0] >> 32),

@@ -40,7 +40,17 @@ constexpr int kWaves = kThreads / 64;
 #endif
 constexpr int kWCap = DF2_TOPK_WCAP;           // candidate slots per wave
 constexpr int kReduceAt = DF2_TOPK_REDUCE_AT;  // list length that triggers a cut
-constexpr int kBufs = 3;        // LDS buffers per wave (two sub-chunks in flight)
+#ifndef DF2_TOPK_BUFS
+#define DF2_TOPK_BUFS 3
+#endif
+constexpr int kBufs = DF2_TOPK_BUFS;  // LDS buffers per wave (kBufs - 1 sub-chunks in flight)
+
+// s_waitcnt vmcnt(N) for a compile-time N (the instruction takes an immediate)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt immediate");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 template <class KT, int NV>
 struct WaveSmem {
@@ -290,26 +300,21 @@ __global__ __launch_bounds__(kThreads) void topk_wave_kernel(
     return true;
   };
 
-  // three buffers: sub-chunks j + 1 and j + 2 are in flight while j is examined. Every
-  // iteration issues exactly NV copies (clamped past the end), so "all but the newest
-  // 2 NV copies have landed" means sub-chunk j is in LDS.
+  // kBufs buffers: sub-chunks j + 1 .. j + kBufs - 1 are in flight while j is examined.
+  // Every iteration issues exactly NV copies (clamped past the end), so "all but the
+  // newest (kBufs - 1) NV copies have landed" means sub-chunk j is in LDS.
   if (threadIdx.x == 0) sm.shared_tf = 0;
   __syncthreads();
-  issue(0, 0);
-  issue(1, 1);
+#pragma unroll
+  for (int i = 0; i < kBufs - 1; ++i) issue(i, i);
   for (int j = 0; j < nsub; ++j) {
     if (j > 0) {
       const uint32_t st = __hip_atomic_load(&sm.shared_tf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       Tf = st > Tf ? st : Tf;
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // sub-chunk j - 1's reads are done
-    issue(j + 2, (j + 2) % kBufs);
-    if constexpr (NV == 1)
-      asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-    else if constexpr (NV == 2)
-      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    issue(j + kBufs - 1, (j + kBufs - 1) % kBufs);
+    wait_vmcnt<(kBufs - 1) * NV>();
     u32x4_t q[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) q[v] = sm.buf[w][j % kBufs][v][lane];
