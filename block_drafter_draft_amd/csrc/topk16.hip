@@ -27,7 +27,10 @@
 namespace df2 {
 namespace {
 
-constexpr int kThreads = kChunkThreads;
+#ifndef DF2_TOPK_THREADS
+#define DF2_TOPK_THREADS 256
+#endif
+constexpr int kThreads = DF2_TOPK_THREADS;  // four waves share an admission threshold
 
 #define DF2_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
@@ -278,10 +281,12 @@ __global__ __launch_bounds__(kThreads) void topk_wave_kernel(
     if (__ballot(kmax >= Tf) == 0) return true;
     const int cnt0_fast = cnt;
     const uint64_t below = (1ull << lane) - 1;
+    // each element position's ballot comes from one 16-bit compare of its half word
+    const uint16_t tf16 = (uint16_t)Tf;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
-      const uint32_t k = (key2[e / 2] >> (16 * (e & 1))) & 0xffffu;
-      const bool take = kmax >= Tf && k >= Tf;
+      const uint16_t k = (e & 1) ? (uint16_t)(key2[e / 2] >> 16) : (uint16_t)key2[e / 2];
+      const bool take = k >= tf16;
       const uint64_t m = __ballot(take);
       if (m) {
         const int pos = cnt + __popcll(m & below);
@@ -479,7 +484,7 @@ void launch_all(const Plan& p, const void* scores, int64_t ss, int64_t rs, int r
                                                              p.nseg, ws);
   const int nlists = p.nseg * kWaves;
   const size_t lds = (size_t)nlists * sizeof(uint64_t);
-  merge16_kernel<ElementValue<KT>><<<B * N, kThreads, lds, st>>>(
+  merge16_kernel<ElementValue<KT>><<<B * N, kMergeThreads, lds, st>>>(
       nlists, ws, idx, val, ElementValue<KT>{sc, ss, rs, row0, N});
 }
 
