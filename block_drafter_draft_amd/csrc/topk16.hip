@@ -279,6 +279,7 @@ __global__ __launch_bounds__(kThreads) void topk_wave_kernel(
       publish();
     }
     if (__ballot(kmax >= Tf) == 0) return true;
+    cnt = __builtin_amdgcn_readfirstlane(cnt);  // wave-uniform: lets the count live in an SGPR
     const int cnt0_fast = cnt;
     const uint64_t below = (1ull << lane) - 1;
     // each element position's ballot comes from one 16-bit compare of its half word
@@ -289,7 +290,9 @@ __global__ __launch_bounds__(kThreads) void topk_wave_kernel(
       const bool take = k >= tf16;
       const uint64_t m = __ballot(take);
       if (m) {
-        const int pos = cnt + __popcll(m & below);
+        // this lane's rank among the takers: a masked bit count of the lanes below it
+        const int pos = cnt + (int)__builtin_amdgcn_mbcnt_hi(
+                                  (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
         if (take && pos < kWCap) {
           const int x = wb + (e / EPV) * 64 * EPV + lane * EPV + (e % EPV);
           list[pos] = pack_cand(k == KT::kNegZeroRaw ? KT::kPosZero : k, (uint32_t)x);
