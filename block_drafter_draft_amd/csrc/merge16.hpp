@@ -46,12 +46,33 @@ __global__ __launch_bounds__(kMergeThreads) void merge16_kernel(int nlists,
   const int rowid = blockIdx.x;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const uint64_t* src = ws + (int64_t)rowid * nlists * kTopK;
+  // A row of at most kRegEntries * 256 entries is loaded whole, in one round trip: thread t
+  // holds entries t, t + 256, ... of the row's lists laid end to end; the holders of each
+  // list's first entry (its maximum) put it in LDS. Longer rows read the maxima first and
+  // then only the lists that can hold winners.
+  constexpr int kRegEntries = 4;
+  const int ne = nlists * kTopK;
+  const bool whole = ne <= kRegEntries * kMergeThreads;
+  uint64_t e[kRegEntries];
   if (t == 0) count = 0;
+  if (whole) {
+#pragma unroll
+    for (int i = 0; i < kRegEntries; ++i) {
+      const int f = t + kMergeThreads * i;
+      e[i] = f < ne ? src[f] : 0ull;
+    }
+#pragma unroll
+    for (int i = 0; i < kRegEntries; ++i) {
+      const int f = t + kMergeThreads * i;
+      if (f < ne && f % kTopK == 0) cmax[f / kTopK] = e[i];
+    }
+    __syncthreads();
+  } else {
+    for (int c = t; c < nlists; c += kMergeThreads) cmax[c] = src[(int64_t)c * kTopK];
+  }
   uint32_t kl = 0;
   for (int c = t; c < nlists; c += kMergeThreads) {
-    const uint64_t v = src[(int64_t)c * kTopK];
-    cmax[c] = v;
-    const uint32_t k = cand_key(v);
+    const uint32_t k = cand_key(cmax[c]);
     kl = k > kl ? k : kl;
   }
   const uint32_t tw = wave_kth16<32>(kl);
@@ -62,18 +83,28 @@ __global__ __launch_bounds__(kMergeThreads) void merge16_kernel(int nlists,
   for (int i = 1; i < kMergeWaves; ++i) Tk = wthr[i] > Tk ? wthr[i] : Tk;
   uint64_t T = (uint64_t)Tk << 32;  // the smallest packed word with key Tk
   for (int pass = 0; pass < 2; ++pass) {
-    for (int c = t; c < nlists; c += kMergeThreads) {
-      if (cmax[c] == 0 || cmax[c] < T) continue;
-      const u32x4_t* l4 = reinterpret_cast<const u32x4_t*>(src + (int64_t)c * kTopK);
-      u32x4_t q[kTopK / 2];
+    if (whole) {
 #pragma unroll
-      for (int i = 0; i < kTopK / 2; ++i) q[i] = l4[i];
-#pragma unroll
-      for (int i = 0; i < kTopK; ++i) {
-        const uint64_t v = ((uint64_t)q[i / 2][2 * (i & 1) + 1] << 32) | q[i / 2][2 * (i & 1)];
-        if (v != 0 && v >= T) {
+      for (int i = 0; i < kRegEntries; ++i) {
+        if (e[i] != 0 && e[i] >= T) {
           const int pos = atomicAdd(&count, 1);
-          if (pos < kMCap) cand[pos] = v;
+          if (pos < kMCap) cand[pos] = e[i];
+        }
+      }
+    } else {
+      for (int c = t; c < nlists; c += kMergeThreads) {
+        if (cmax[c] == 0 || cmax[c] < T) continue;
+        const u32x4_t* l4 = reinterpret_cast<const u32x4_t*>(src + (int64_t)c * kTopK);
+        u32x4_t q[kTopK / 2];
+#pragma unroll
+        for (int i = 0; i < kTopK / 2; ++i) q[i] = l4[i];
+#pragma unroll
+        for (int i = 0; i < kTopK; ++i) {
+          const uint64_t v = ((uint64_t)q[i / 2][2 * (i & 1) + 1] << 32) | q[i / 2][2 * (i & 1)];
+          if (v != 0 && v >= T) {
+            const int pos = atomicAdd(&count, 1);
+            if (pos < kMCap) cand[pos] = v;
+          }
         }
       }
     }
