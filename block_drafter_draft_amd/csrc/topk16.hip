@@ -308,6 +308,60 @@ __global__ __launch_bounds__(kThreads) void topk_wave_kernel(
     return true;
   };
 
+  // Once the threshold key is above +0, only positive values can be admitted, and raw
+  // bf16 bits decide: positive values order like their bits read as signed 16-bit
+  // integers, and every negative value reads below them. So one signed packed maximum gives
+  // a lane's largest positive value, and one unsigned packed maximum finds -inf or a
+  // negative NaN (bits >= 0xff80); a positive NaN or +inf shows as a signed maximum
+  // >= 0x7f80. Two VALU operations per two elements, against four for the keys. Returns
+  // false, as process_bf16 does, when the sub-chunk must go the exact way.
+  auto process_bf16_pos = [&](const u32x4_t (&q)[NV], int j) -> bool {
+    typedef short i16x2_t __attribute__((ext_vector_type(2)));
+    typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+    const int wb = wbase(j);
+    i16x2_t smx = {-32768, -32768};
+    u16x2_t umx = {0, 0};
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // (through a named word: a bit cast of a vector element itself compiled to a read
+        // of element 0 only)
+        const uint32_t u = q[v][i];
+        smx = __builtin_elementwise_max(smx, __builtin_bit_cast(i16x2_t, u));
+        umx = __builtin_elementwise_max(umx, __builtin_bit_cast(u16x2_t, u));
+      }
+    const int smax = smx[0] > smx[1] ? smx[0] : smx[1];
+    const uint32_t umax = umx[0] > umx[1] ? umx[0] : umx[1];
+    if (__ballot(smax >= 0x7f80 || umax >= 0xff80u)) return false;
+    const int traw = (int)(Tf ^ 0x8000u);  // the threshold as raw bits of a positive value
+    if (__ballot(smax >= traw) == 0) return true;
+    cnt = __builtin_amdgcn_readfirstlane(cnt);
+    const int cnt0_pos = cnt;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const uint32_t wd = q[e / EPV][(e % EPV) / 2];
+      const int r = (e & 1) ? ((int)wd >> 16) : (int)(int16_t)(wd & 0xffffu);
+      const bool take = r >= traw;
+      const uint64_t m = __ballot(take);
+      if (m) {
+        const int pos = cnt + (int)__builtin_amdgcn_mbcnt_hi(
+                                  (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (take && pos < kWCap) {
+          const int x = wb + (e / EPV) * 64 * EPV + lane * EPV + (e % EPV);
+          list[pos] = pack_cand((uint32_t)r | 0x8000u, (uint32_t)x);  // a positive value's key
+        }
+        cnt += __popcll(m);
+      }
+    }
+    if (cnt > kWCap) {
+      cnt = cnt0_pos;  // the kept list is intact below cnt0_pos
+      return false;
+    }
+    if (cnt > kReduceAt) shrink();
+    return true;
+  };
+
   // kBufs buffers: sub-chunks j + 1 .. j + kBufs - 1 are in flight while j is examined.
   // Every iteration issues exactly NV copies (clamped past the end), so "all but the
   // newest (kBufs - 1) NV copies have landed" means sub-chunk j is in LDS.
@@ -328,8 +382,14 @@ __global__ __launch_bounds__(kThreads) void topk_wave_kernel(
     for (int v = 0; v < NV; ++v) q[v] = sm.buf[w][j % kBufs][v][lane];
     const bool whole = wbase(j) + WCH <= s1;
     bool done = false;
-    if constexpr (sizeof(E) == 2)
-      if (whole) done = process_bf16(q, j);
+    if constexpr (sizeof(E) == 2) {
+      if (whole) {
+        if (j > 0 && __builtin_amdgcn_readfirstlane(Tf) > KT::kPosZero)
+          done = process_bf16_pos(q, j);
+        else
+          done = process_bf16(q, j);
+      }
+    }
     if (!done) {
       uint32_t bits[EPT];
 #pragma unroll
