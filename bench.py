@@ -443,6 +443,23 @@ class Bench:
 
         # Verify alone where every proposal is accepted: greedy sequences then need all
         # N + 1 rows, sampled ones the bonus row. The other extreme from the step's targets.
+        rec["verify_all_accept"] = None if args.no_all_accept else self._all_accept(cfg, wl, runner, reps, temps)
+        if not args.no_lmhead:
+            rec["lmhead_topk16"] = self._lmhead(cfg, wl)
+            rec["proj"] = self._proj(cfg, wl, inputs, nsets) if cfg.act_bf16 else None
+        if not args.no_q8:
+            rec["select_q8"] = self._q8(cfg, wl, cb, inputs, runner, nsets, reps,
+                                        stage_ms["select"])
+            rec["ddtree"] = self._ddtree(cfg, inputs, runner, nsets, reps)
+        del graphs, runner, inputs
+        torch.cuda.empty_cache()
+        return rec, cfg
+
+    def _all_accept(self, cfg, wl, runner, reps, temps):
+        import numpy as np
+        torch, dev = self.torch, self.dev
+        from block_drafter_draft_amd import dflash2 as d2
+        B, P, N, V = cfg.B, cfg.P, cfg.N, cfg.V
         vi = wl.all_accept_verify_inputs(cfg)
         vt = torch.from_numpy(vi.target.view(np.int16) if vi.target.dtype == np.uint16
                               else vi.target)
@@ -462,23 +479,12 @@ class Bench:
         n_all = va_n.cpu().numpy()
         va_ms = self.timed(verify_acc_call, reps)
         va_bytes = verify_bytes(cfg, n_all, temps)
-        rec["verify_all_accept"] = {
+        return {
             "mean_accepted": float(n_all.mean()), "us_per_call": va_ms * 1e3,
             "bytes_per_call": float(va_bytes),
             "achieved": va_bytes / (va_ms * 1e-3) / 1e9,
             "frac": va_bytes / (va_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
-        del vt
 
-        if not args.no_lmhead:
-            rec["lmhead_topk16"] = self._lmhead(cfg, wl)
-            rec["proj"] = self._proj(cfg, wl, inputs, nsets) if cfg.act_bf16 else None
-        if not args.no_q8:
-            rec["select_q8"] = self._q8(cfg, wl, cb, inputs, runner, nsets, reps,
-                                        stage_ms["select"])
-            rec["ddtree"] = self._ddtree(cfg, inputs, runner, nsets, reps)
-        del graphs, runner, inputs
-        torch.cuda.empty_cache()
-        return rec, cfg
 
     # The output-head projection fused with the top-16 (a call outside the step): the
     # drafter's rows 1..N against a synthetic V x C bf16 head, ~N(0, 1/C), generated on the
@@ -635,6 +641,9 @@ def main():
                     help="skip the separate output-head + top-16 and projection measurements")
     ap.add_argument("--no-q8", action="store_true",
                     help="skip the separate Q8-selector and draft-tree measurements")
+    ap.add_argument("--no-all-accept", action="store_true",
+                    help="skip verify on all-accept inputs (keeps per-dispatch profiles of the "
+                         "step's own verify calls unmixed)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
 
