@@ -36,6 +36,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
 LLC_BYTES = 256 << 20           # last-level (MALL) cache
+COLD_PASS = 3                   # a loop over distinct inputs reads this many LLCs per pass
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -285,7 +286,7 @@ class Bench:
         from block_drafter_draft_amd.step import DeviceInputs, StepRunner
         args, dev = self.args, self.dev
         cfg = wl.CONFIGS[wid]
-        nsets = args.sets or max(1, min(16, math.ceil(1.25 * LLC_BYTES / set_bytes(cfg))))
+        nsets = args.sets or max(1, min(32, math.ceil(COLD_PASS * LLC_BYTES / set_bytes(cfg))))
         log(f"workload {cfg.cfg} ({cfg.name}), {nsets} input set(s) of "
             f"{set_bytes(cfg) / 1e6:.1f} MB")
         cb = wl.codebooks(cfg)
@@ -331,28 +332,6 @@ class Bench:
                           x.v_ring[layer], x.ctx_len, cfg.W, out=o.attn[layer],
                           ws=runner.ws_attn)
 
-        def conv_call(r):
-            x = inputs[r % nsets]
-            s = (r // nsets) % cfg.sites
-            d2.dynconv2(x.conv_x[s], x.conv_base[s], x.conv_delta[s], out=o.conv[s])
-
-        def topk_call(r):
-            x = inputs[r % nsets]
-            d2.topk16(x.draft, B, N, 1, P * V, V, V, idx=o.cand_idx, val=o.cand_val,
-                      ws=runner.ws_topk)
-
-        def select_call(r):
-            x = inputs[r % nsets]
-            d2.select(o.cand_idx, o.cand_val, x.gate, x.pred_cb, x.succ_cb, x.anchor,
-                      x.temperature, cfg.seed, r, tokens=o.tokens, slot=o.slot, q=o.q,
-                      status=o.status, ws=runner.ws_sel)
-
-        def verify_call(r):
-            x = inputs[r % nsets]
-            d2.verify(x.target, B, N, P * V, V, V, o.tokens, o.cand_idx, o.q, o.slot,
-                      x.temperature, cfg.seed, r, o.status, n_accept=o.n_accept,
-                      out_tokens=o.out_tokens, ws=runner.ws_ver)
-
         # accept counts of every input set's step, with the counter each graph uses
         n_acc_sets = []
         for i in range(nsets):
@@ -360,18 +339,80 @@ class Bench:
             n_acc_sets.append(o.n_accept.cpu().numpy().copy())
         runner.run(0, 0)
         torch.cuda.synchronize()
+        sb = stage_bytes(cfg, n_acc_sets)
+        sb["verify"] = verify_bytes(cfg, n_acc_sets[0], cfg.temperatures())  # timed on set 0
+
+        # In the step every stage reads its inputs from HBM: the step's working set is many
+        # times the last-level cache. So that a loop of one stage's calls does the same,
+        # each loop cycles through enough distinct copies of that stage's inputs (stacked,
+        # the given sets first, then clones of them in turn) to read COLD_PASS times the
+        # cache per pass.
+        def n_cold(per_call_bytes):
+            return max(1, math.ceil(COLD_PASS * LLC_BYTES / max(per_call_bytes, 1)))
+
+        def stack(srcs, n):
+            out = torch.empty((n, *srcs[0].shape), dtype=srcs[0].dtype, device=dev)
+            for k in range(n):
+                out[k].copy_(srcs[k % len(srcs)])
+            return out
+
+        sites = cfg.sites
+        nc = n_cold(sb["dynconv2"])
+        cx = stack([x.conv_x[s] for x in inputs for s in range(sites)], nc)
+        cbase = stack([x.conv_base[s] for x in inputs for s in range(sites)], nc)
+        cdel = stack([x.conv_delta[s] for x in inputs for s in range(sites)], nc)
+
+        def conv_call(r):
+            d2.dynconv2(cx[r % nc], cbase[r % nc], cdel[r % nc], out=o.conv[r % sites])
+
+        nt = n_cold(sb["topk16"])
+        drafts = stack([x.draft for x in inputs], nt)
+
+        def topk_call(r):
+            d2.topk16(drafts[r % nt], B, N, 1, P * V, V, V, idx=o.cand_idx, val=o.cand_val,
+                      ws=runner.ws_topk)
+
+        # the selector gathers codebook rows chosen by the candidates: copies of the
+        # codebooks, and per call the candidate indices shifted by a multiple of a stride,
+        # so that each call gathers other rows
+        ncb = n_cold(inputs[0].pred_cb.numel() * inputs[0].pred_cb.element_size() * 2)
+        cbs = [(inputs[0].pred_cb, inputs[0].succ_cb)] + [
+            (inputs[0].pred_cb.clone(), inputs[0].succ_cb.clone()) for _ in range(ncb - 1)]
+        ns = n_cold(sb["select"])
+        cand0 = o.cand_idx.clone()
+        cands = torch.stack([(cand0 + 7919 * k) % V for k in range(ns)]).to(torch.int32)
+
+        def select_call(r):
+            x = inputs[r % nsets]
+            pc, sc = cbs[r % ncb]
+            d2.select(cands[r % ns], o.cand_val, x.gate, pc, sc, x.anchor,
+                      x.temperature, cfg.seed, r, tokens=o.tokens, slot=o.slot, q=o.q,
+                      status=o.status, ws=runner.ws_sel)
+
+        nv = n_cold(sb["verify"])
+        targets = stack([inputs[0].target], nv)
+
+        def verify_call(r):
+            x = inputs[0]
+            d2.verify(targets[r % nv], B, N, P * V, V, V, o.tokens, o.cand_idx, o.q, o.slot,
+                      x.temperature, cfg.seed, r, o.status, n_accept=o.n_accept,
+                      out_tokens=o.out_tokens, ws=runner.ws_ver)
+
+        torch.cuda.synchronize()
         stage_ms = {"block_attn": self.timed(attn_call, attn_calls),
-                    "dynconv2": self.timed(conv_call, conv_calls),
-                    "topk16": self.timed(topk_call, reps),
-                    "select": self.timed(select_call, reps),
-                    "verify": self.timed(verify_call, reps)}
+                    "dynconv2": self.timed(conv_call, max(nc, conv_calls)),
+                    "topk16": self.timed(topk_call, max(nt, reps)),
+                    "select": self.timed(select_call, max(ns, ncb, reps))}
+        runner.run(0, 0)  # verify reads set 0's own proposals
+        stage_ms["verify"] = self.timed(verify_call, max(nv, reps))
+        cold_copies = {"dynconv2": nc, "topk16": nt, "select": [ns, ncb], "verify": nv}
+        del cx, cbase, cdel, drafts, cbs, cands, targets
         attn_ms = stage_ms["block_attn"]
         per_set = [attn_bytes_flops(cfg, x.ctx_len.cpu().numpy()) for x in inputs]
         a_bytes = sum(p[0] for p in per_set) / len(per_set)
         a_flops = sum(p[1] for p in per_set) / len(per_set)
         achieved = a_bytes / (attn_ms * 1e-3) / 1e9
 
-        sb = stage_bytes(cfg, n_acc_sets)
         stage_hbm = {"block_attn": {"bytes_per_call": a_bytes, "achieved": achieved,
                                     "frac": achieved / HBM_PEAK_GBS}}
         for k, nb in sb.items():
@@ -403,6 +444,7 @@ class Bench:
             "step_ms": {"median": pct(step_ms, 50), "p10": pct(step_ms, 10),
                         "p90": pct(step_ms, 90), "event_mean": ev_total / steps},
             "stage_us": {k: v * 1e3 for k, v in stage_ms.items()},
+            "stage_cold_copies": cold_copies,
             "stage_hbm": stage_hbm,
             "acceptance": acceptance,
         }

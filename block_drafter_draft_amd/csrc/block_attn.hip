@@ -25,6 +25,12 @@
 // f32 path: a plain VALU kernel (one wave per query row), used for small f32 problems.
 #include "common.hpp"
 
+// Split partials stored nontemporally (1) or through L2 (0); the combine kernel reads them
+// right after.
+#ifndef DF2_ATTN_NT_PARTIAL
+#define DF2_ATTN_NT_PARTIAL 0
+#endif
+
 namespace df2 {
 namespace {
 
@@ -291,7 +297,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
                              ((uint32_t)f32_to_bf16(o[i][4 * a + 1] * inv) << 16);
         const uint32_t hi2 = (uint32_t)f32_to_bf16(o[i][4 * a + 2] * inv) |
                              ((uint32_t)f32_to_bf16(o[i][4 * a + 3] * inv) << 16);
-        *reinterpret_cast<uint2*>(dst + d) = make_uint2(lo2, hi2);
+        store_nt(reinterpret_cast<u32x2_t*>(dst + d), u32x2_t{lo2, hi2});
       }
     return;
   }
@@ -617,14 +623,21 @@ __global__ __launch_bounds__(64 * NW) void attn_stream_kernel(
       pk[h >> 2][h & 3] = (uint32_t)f32_to_bf16(acc[2 * h] * inv) |
                           ((uint32_t)f32_to_bf16(acc[2 * h + 1] * inv) << 16);
 #pragma unroll
-    for (int v = 0; v < CPL / 8; ++v) *reinterpret_cast<u32x4_t*>(dst + 8 * v) = pk[v];
+    for (int v = 0; v < CPL / 8; ++v) store_nt(reinterpret_cast<u32x4_t*>(dst + 8 * v), pk[v]);
     return;
   }
   const int64_t part = ((int64_t)b * Hkv + g) * nsplit + split;
   float* po = ws_o + (part * kRows + n) * D + d0;
 #pragma unroll
-  for (int e = 0; e < CPL; e += 4)
+  for (int e = 0; e < CPL; e += 4) {
+#if DF2_ATTN_NT_PARTIAL
+    store_nt(reinterpret_cast<u32x4_t*>(po + e),
+             u32x4_t{__float_as_uint(acc[e]), __float_as_uint(acc[e + 1]),
+                     __float_as_uint(acc[e + 2]), __float_as_uint(acc[e + 3])});
+#else
     *reinterpret_cast<float4*>(po + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+#endif
+  }
   if (w == 0 && hh == 0) ws_ml[part * kRows + n] = make_float2(M, Lsum);
 }
 
@@ -689,7 +702,7 @@ __global__ __launch_bounds__(kRows * CPW / 4) void attn_combine_kernel(
   uint16_t* dst = out + (((int64_t)b * P + slot) * Hq + head) * D + d;
   const uint32_t lo2 = (uint32_t)f32_to_bf16(acc.x * inv) | ((uint32_t)f32_to_bf16(acc.y * inv) << 16);
   const uint32_t hi2 = (uint32_t)f32_to_bf16(acc.z * inv) | ((uint32_t)f32_to_bf16(acc.w * inv) << 16);
-  *reinterpret_cast<uint2*>(dst) = make_uint2(lo2, hi2);
+  store_nt(reinterpret_cast<u32x2_t*>(dst), u32x2_t{lo2, hi2});
 }
 
 template <int D, int CPW>

@@ -12,6 +12,13 @@ namespace df2 {
 constexpr int kTopK = 16;  // candidates per block position
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Results that nothing in the same launch reads again are stored nontemporally: written
+// through rather than left dirty in L2, where the end-of-kernel release would have to
+// write them back before the next kernel may start.
+__device__ __forceinline__ void store_nt(u32x4_t* p, u32x4_t v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void store_nt(u32x2_t* p, u32x2_t v) { __builtin_nontemporal_store(v, p); }
 
 // ---------------------------------------------------------------------------------------
 // Element types

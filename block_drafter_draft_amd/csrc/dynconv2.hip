@@ -10,7 +10,8 @@
 // rows and the two coefficients of its group, all independent of each other and issued
 // together, so a call is one memory round trip. The neighbour row is re-read from L2, not HBM. The op moves
 // B*P*C*(2+2) bytes plus the base and coefficients and is bound by memory (or by launch
-// latency at small B).
+// latency at small B). The output is stored nontemporally: left dirty in L2, its
+// write-back at the end of the kernel cost about 2 us per call at batch 64.
 #include "common.hpp"
 
 namespace df2 {
@@ -77,11 +78,13 @@ __global__ __launch_bounds__(kConvThreads) void dynconv2_kernel(const void* __re
 #pragma unroll
     for (int h = 0; h < 4; ++h)
       o[h] = (uint32_t)f32_to_bf16(y[2 * h]) | ((uint32_t)f32_to_bf16(y[2 * h + 1]) << 16);
-    *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(out) + (int64_t)row * C + c0) = o;
+    store_nt(reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(out) + (int64_t)row * C + c0), o);
   } else {
-    float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + (int64_t)row * C + c0);
-    p[0] = make_float4(y[0], y[1], y[2], y[3]);
-    p[1] = make_float4(y[4], y[5], y[6], y[7]);
+    u32x4_t* p = reinterpret_cast<u32x4_t*>(reinterpret_cast<float*>(out) + (int64_t)row * C + c0);
+    store_nt(p, u32x4_t{__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]),
+                        __float_as_uint(y[3])});
+    store_nt(p + 1, u32x4_t{__float_as_uint(y[4]), __float_as_uint(y[5]), __float_as_uint(y[6]),
+                            __float_as_uint(y[7])});
   }
 }
 

@@ -202,10 +202,11 @@ __device__ __forceinline__ uint64_t chunk_best_full(const uint32_t (&bits)[EPT],
   return 0ull;  // not reached: some lane holds M
 }
 
-// Grid: (chunks, sequences). A greedy sequence's workgroup reduces its chunk of row 0; a
-// sampled sequence's workgroup recomputes the accept chain and sums its chunk of the row the
-// draw comes from.
-template <class KT, int EPT, bool VEC>
+// Grid: (units of CPW chunks, sequences). A greedy sequence's workgroup reduces its chunks
+// of row 0; a sampled sequence's workgroup recomputes the accept chain and sums its chunks
+// of the row the draw comes from. Every chunk's loads are issued before any is used, so a
+// sampled workgroup spends the chain's dependent round trips once for CPW chunks.
+template <class KT, int EPT, bool VEC, int CPW>
 __global__ __launch_bounds__(kThreads) void verify_rows_kernel(
     const typename KT::elem_t* __restrict__ target, int64_t seq_stride, int64_t row_stride, int V,
     const int32_t* __restrict__ tokens, const int32_t* __restrict__ cidx,
@@ -213,10 +214,11 @@ __global__ __launch_bounds__(kThreads) void verify_rows_kernel(
     const float* __restrict__ temperature, uint64_t seed, uint64_t step, int N, int nchunks,
     Ws ws) {
   constexpr int CH = EPT * kThreads;
-  const int chunk = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
-  const int base = chunk * CH;
+  const int unit = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  const int c0 = unit * CPW;                      // first chunk of this workgroup
+  const int nc = min(CPW, nchunks - c0);          // its chunks (>= 1)
   __shared__ ChainRec rec;
-  __shared__ uint64_t red[kThreads / 64][2];
+  __shared__ uint64_t red[kThreads / 64][CPW][2];
   __shared__ int redf[kThreads / 64];
 
   // a sampled chain's first loads do not depend on the temperature: issue them with it
@@ -243,24 +245,35 @@ __global__ __launch_bounds__(kThreads) void verify_rows_kernel(
 
   if (mode == 0) {
     // kernel 2's row words and arrival counter for this sequence start at zero
-    if (chunk == 0 && t < kRowWords) {
+    if (unit == 0 && t < kRowWords) {
       store_agent(ws.rowmax + (int64_t)b * kRowWords + t, 0ull);
       if (t == 0) store_agent(ws.arrive + b, 0u);
     }
-    uint32_t bits[EPT];
-    const bool full = VEC && base + CH <= V;
-    if (full)
-      load_chunk_full<KT, EPT>(tb, base, bits);
-    else
-      load_chunk<KT, EPT, VEC>(tb, base, V, bits);
-    const uint64_t m = full ? chunk_best_full<KT, EPT>(bits, base, V)
-                            : chunk_best_exact<KT, EPT, VEC>(bits, base, V);
-    if ((t & 63) == 0) red[t >> 6][0] = m;
+    uint32_t bits[CPW][EPT];
+#pragma unroll
+    for (int cc = 0; cc < CPW; ++cc) {
+      const int base = (c0 + cc) * CH;
+      if (cc < nc) {
+        if (VEC && base + CH <= V)
+          load_chunk_full<KT, EPT>(tb, base, bits[cc]);
+        else
+          load_chunk<KT, EPT, VEC>(tb, base, V, bits[cc]);
+      }
+    }
+#pragma unroll
+    for (int cc = 0; cc < CPW; ++cc) {
+      const int base = (c0 + cc) * CH;
+      uint64_t m = 0;
+      if (cc < nc)
+        m = (VEC && base + CH <= V) ? chunk_best_full<KT, EPT>(bits[cc], base, V)
+                                    : chunk_best_exact<KT, EPT, VEC>(bits[cc], base, V);
+      if ((t & 63) == 0) red[t >> 6][cc][0] = m;
+    }
     __syncthreads();
-    if (t == 0) {
-      uint64_t g = red[0][0];
-      for (int w = 1; w < kThreads / 64; ++w) g = red[w][0] > g ? red[w][0] : g;
-      ws.best0[(int64_t)b * nchunks + chunk] = g;
+    if (t < nc) {
+      uint64_t g = red[0][t][0];
+      for (int w = 1; w < kThreads / 64; ++w) g = red[w][t][0] > g ? red[w][t][0] : g;
+      ws.best0[(int64_t)b * nchunks + c0 + t] = g;
     }
     return;
   }
@@ -272,17 +285,25 @@ __global__ __launch_bounds__(kThreads) void verify_rows_kernel(
     allq[t] = q_pre;
   }
   accept_chain(tgt, row_stride, V, N, x_pre, sl_pre, allc, allq, seed, step, b, &rec);
-  if (chunk == 0 && t == 0) ws.chain[b] = rec;
+  if (unit == 0 && t == 0) ws.chain[b] = rec;
   const float* row = tgt + (int64_t)(rec.pos - 1) * row_stride;
 
-  uint32_t bits[EPT];
-  if (VEC && base + CH <= V)
-    load_chunk_full<KT, EPT>(reinterpret_cast<const typename KT::elem_t*>(row), base, bits);
-  else
-    load_chunk<KT, EPT, VEC>(reinterpret_cast<const typename KT::elem_t*>(row), base, V, bits);
-  // residual corrections for the candidates of slot pos that fall in this chunk; for a
-  // repeated index only its first occurrence counts. Their gathers go out with the chunk.
+  uint32_t bits[CPW][EPT];
+#pragma unroll
+  for (int cc = 0; cc < CPW; ++cc) {
+    const int base = (c0 + cc) * CH;
+    if (cc < nc) {
+      if (VEC && base + CH <= V)
+        load_chunk_full<KT, EPT>(reinterpret_cast<const typename KT::elem_t*>(row), base, bits[cc]);
+      else
+        load_chunk<KT, EPT, VEC>(reinterpret_cast<const typename KT::elem_t*>(row), base, V,
+                                 bits[cc]);
+    }
+  }
+  // residual corrections for the candidates of slot pos that fall in these chunks; for a
+  // repeated index only its first occurrence counts. Their gathers go out with the chunks.
   bool corr = false;
+  int corr_cc = 0;
   float p_c = 0.0f, q_c = 0.0f;
   if (rec.resid && t < kTopK) {
     const int32_t* ci = allc + (rec.pos - 1) * kTopK;
@@ -291,18 +312,26 @@ __global__ __launch_bounds__(kThreads) void verify_rows_kernel(
 #pragma unroll
     for (int k = 0; k < kTopK; ++k)
       if (k < t) first = first && ci[k] != c;
-    if (first && c >= base && c < base + CH) {
+    if (first && c >= c0 * CH && c < (c0 + nc) * CH) {
       corr = true;
+      corr_cc = c / CH - c0;
       p_c = row[c];
       q_c = allq[(rec.pos - 1) * kTopK + t];
     }
   }
-  uint64_t zp = 0;
   int fl = 0;
+  uint64_t zp[CPW];
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    const int x = index_of<EPT, VEC, KT>(base, e);
-    if (x < V) zp += quant40(prob_ok(__uint_as_float(bits[e]), &fl));
+  for (int cc = 0; cc < CPW; ++cc) {
+    const int base = (c0 + cc) * CH;
+    zp[cc] = 0;
+    if (cc < nc) {
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        const int x = index_of<EPT, VEC, KT>(base, e);
+        if (x < V) zp[cc] += quant40(prob_ok(__uint_as_float(bits[cc][e]), &fl));
+      }
+    }
   }
   int64_t dz = 0;
   if (corr) {
@@ -312,27 +341,30 @@ __global__ __launch_bounds__(kThreads) void verify_rows_kernel(
     const float d = __fsub_rn(p, qk);
     dz = (int64_t)quant40(d > 0.0f ? d : 0.0f) - (int64_t)quant40(p);
   }
-  uint64_t zr = zp + (uint64_t)dz;
-  zp = wave_sum_u64_all(zp, t & 63);  // every lane is active here
-  zr = wave_sum_u64_all(zr, t & 63);
   fl = wave_or(fl);
-  if ((t & 63) == 0) {
-    red[t >> 6][0] = zr;
-    red[t >> 6][1] = zp;
-    redf[t >> 6] = fl;
+#pragma unroll
+  for (int cc = 0; cc < CPW; ++cc) {
+    uint64_t zr = zp[cc] + (corr && corr_cc == cc ? (uint64_t)dz : 0ull);
+    const uint64_t sp = wave_sum_u64_all(zp[cc], t & 63);  // every lane is active here
+    zr = wave_sum_u64_all(zr, t & 63);
+    if ((t & 63) == 0) {
+      red[t >> 6][cc][0] = zr;
+      red[t >> 6][cc][1] = sp;
+    }
   }
+  if ((t & 63) == 0) redf[t >> 6] = fl;
   __syncthreads();
-  if (t == 0) {
+  if (t < nc) {
     uint64_t a = 0, c = 0;
     int f = 0;
     for (int w = 0; w < kThreads / 64; ++w) {
-      a += red[w][0];
-      c += red[w][1];
+      a += red[w][t][0];
+      c += red[w][t][1];
       f |= redf[w];
     }
-    ws.zsum[((int64_t)b * nchunks + chunk) * 2 + 0] = a;
-    ws.zsum[((int64_t)b * nchunks + chunk) * 2 + 1] = c;
-    ws.zflag[(int64_t)b * nchunks + chunk] = f;
+    ws.zsum[((int64_t)b * nchunks + c0 + t) * 2 + 0] = a;
+    ws.zsum[((int64_t)b * nchunks + c0 + t) * 2 + 1] = c;
+    ws.zflag[(int64_t)b * nchunks + c0 + t] = f;
   }
 }
 
@@ -733,8 +765,18 @@ constexpr int kEPT = 8;  // elements per thread: one 16-byte bf16 vector or two 
 struct Plan {
   int nchunks;
   bool vec;
-  int G;  // kernel-2 workgroups per sequence
+  int G;    // kernel-2 workgroups per sequence
+  int cpw;  // kernel-1 chunks per workgroup
 };
+
+// Kernel-1 chunks per workgroup (1, 2 or 4): a chunk is 8 KB of an f32 row, and a sampled
+// workgroup spends its chain's dependent round trips before its row loads, so larger
+// grids take two chunks per workgroup. Measured at batch 64 (7,808 chunks, cold rows):
+// kernel 1 alone 18.3 us with one chunk per workgroup, 16.5 with two, 18.5 with four; at
+// batch 1 one chunk is fastest. DF2_VERIFY_CPW fixes the value; 0 chooses by grid size.
+#ifndef DF2_VERIFY_CPW
+#define DF2_VERIFY_CPW 0
+#endif
 
 // Kernel 2 workgroups per sequence: one per chunk by default (0), so that even a single
 // accepted greedy chain streams rows 1..N over the whole chip in one or two round trips;
@@ -752,6 +794,8 @@ Plan make_plan(int B, int V, int dtype, const void* target, int64_t ss, int64_t 
   p.nchunks = (V + kEPT * kThreads - 1) / (kEPT * kThreads);
   p.G = kFinishTargetWGs ? std::max(1, std::min(p.nchunks, kFinishTargetWGs / B)) : p.nchunks;
   p.G = (int)std::min<int64_t>(p.G, INT32_MAX / B);  // the 1-D grid of B * G workgroups
+  const int64_t wgs = (int64_t)B * p.nchunks;
+  p.cpw = DF2_VERIFY_CPW ? DF2_VERIFY_CPW : (wgs >= 1024 ? 2 : 1);
   const int esz = dtype == DFLASH2_BF16 ? 2 : 4;
   p.vec = (target == nullptr || aligned(target, 16)) && (ss * esz) % 16 == 0 && (rs * esz) % 16 == 0;
   return p;
@@ -763,8 +807,16 @@ void launch(const Plan& p, const void* target, int64_t ss, int64_t rs, int V,
             const float* temp, uint64_t seed, uint64_t step, int B, int N, Ws w, int32_t* n_acc,
             int32_t* out, int32_t* status, hipStream_t st) {
   using E = typename KT::elem_t;
-  verify_rows_kernel<KT, kEPT, VEC><<<dim3(p.nchunks, B), kThreads, 0, st>>>(
-      (const E*)target, ss, rs, V, tokens, cidx, q, slot, temp, seed, step, N, p.nchunks, w);
+  const dim3 g1((p.nchunks + p.cpw - 1) / p.cpw, B);
+  if (p.cpw >= 4)
+    verify_rows_kernel<KT, kEPT, VEC, 4><<<g1, kThreads, 0, st>>>(
+        (const E*)target, ss, rs, V, tokens, cidx, q, slot, temp, seed, step, N, p.nchunks, w);
+  else if (p.cpw == 2)
+    verify_rows_kernel<KT, kEPT, VEC, 2><<<g1, kThreads, 0, st>>>(
+        (const E*)target, ss, rs, V, tokens, cidx, q, slot, temp, seed, step, N, p.nchunks, w);
+  else
+    verify_rows_kernel<KT, kEPT, VEC, 1><<<g1, kThreads, 0, st>>>(
+        (const E*)target, ss, rs, V, tokens, cidx, q, slot, temp, seed, step, N, p.nchunks, w);
   verify_finish_kernel<KT, kEPT, VEC><<<dim3(B * p.G), kThreads, 0, st>>>(
       (const E*)target, ss, rs, V, tokens, cidx, q, temp, seed, step, N, p.nchunks, p.G, w, n_acc,
       out, status);
