@@ -196,3 +196,33 @@ def test_topk16_long_rows_adversarial(d2, case):
                 for p_, v_ in zip(pos, pats):
                     bits[b, r, p_] = v_
     check(d2, host, B, N, 1, (N + 1) * V, V, V, f"long rows {case}")
+
+
+def test_topk16_shared_workspace(d2):
+    # One workspace for many calls with different rows, starting from stale contents.
+    B, N, V = 8, 7, 100003
+    rng = np.random.default_rng(71)
+    ws = d2.workspace(d2.topk16_workspace_bytes(B, N, V, d2.F32), DEV)
+    ws.fill_(0xA5)
+    for it in range(6):
+        say(f"topk16 shared workspace call {it} B={B} N={N} V={V}")
+        host = rng.standard_normal((B, N + 1, V)).astype(np.float32)
+        if it % 2:
+            host[:, :, ::7] = 0.5                 # a plateau of ties
+        dev = to_dev(host.reshape(-1))
+        idx = poison_like((B, N, 16), torch.int32)
+        val = poison_like((B, N, 16), torch.float32)
+        d2.topk16(dev, B, N, 1, (N + 1) * V, V, V, idx=idx, val=val, ws=ws)
+        torch.cuda.synchronize()
+        oi, ov = orc.topk16(host.reshape(-1), B, N, 1, (N + 1) * V, V, V)
+        np.testing.assert_array_equal(to_host(idx), oi, err_msg=f"call {it}")
+        assert_same_floats(to_host(val), ov, f"call {it}")
+
+
+@pytest.mark.parametrize("V", [2097152, 2097153])
+def test_topk16_most_lists_per_row(d2, V):
+    # A single row long enough that its 512 workgroups write 2048 lists, which the merge
+    # reads maxima first, and one element past that (513 workgroups).
+    rng = np.random.default_rng(V % 97)
+    host = _bf16(rng.standard_normal((1, 2, V)).astype(np.float32) * 3.0)
+    check(d2, host, 1, 1, 1, 2 * V, V, V, f"most lists V={V}")
