@@ -351,10 +351,9 @@ class Bench:
             return max(1, math.ceil(COLD_PASS * LLC_BYTES / max(per_call_bytes, 1)))
 
         def stack(srcs, n):
-            out = torch.empty((n, *srcs[0].shape), dtype=srcs[0].dtype, device=dev)
-            for k in range(n):
-                out[k].copy_(srcs[k % len(srcs)])
-            return out
+            base = torch.stack(srcs)
+            reps = -(-n // len(srcs))
+            return base.repeat(reps, *([1] * (base.dim() - 1)))[:n].contiguous()
 
         sites = cfg.sites
         nc = n_cold(sb["dynconv2"])
@@ -380,7 +379,8 @@ class Bench:
             (inputs[0].pred_cb.clone(), inputs[0].succ_cb.clone()) for _ in range(ncb - 1)]
         ns = n_cold(sb["select"])
         cand0 = o.cand_idx.clone()
-        cands = torch.stack([(cand0 + 7919 * k) % V for k in range(ns)]).to(torch.int32)
+        shift = 7919 * torch.arange(ns, device=dev, dtype=torch.int64).view(-1, 1, 1, 1)
+        cands = ((cand0.to(torch.int64).unsqueeze(0) + shift) % V).to(torch.int32)
 
         def select_call(r):
             x = inputs[r % nsets]

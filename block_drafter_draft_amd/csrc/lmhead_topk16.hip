@@ -314,18 +314,26 @@ struct TlCursor {
   }
 };
 
+// Grid: 1-D, nwg workgroups per pass over the head times npass passes of 128 hidden rows.
+// The passes of one workgroup slot x run on the same XCD, dispatched eight apart (index
+// (x / 8) 8 npass + 8 p + x % 8; the hardware deals workgroups to the 8 XCDs by index),
+// so they stream the same head tiles at about the same time and the XCD's L2 serves all
+// but the first read.
 __global__ __launch_bounds__(64 * kLmWaves) void lmhead_tiled_kernel(
     const uint16_t* __restrict__ hid, int64_t hss, int64_t hrs, int row0, int N, int M,
-    const uint16_t* __restrict__ wt, int C, int V, int ngroups, uint64_t* __restrict__ lists) {
+    const uint16_t* __restrict__ wt, int C, int V, int ngroups, int nwg, int npass,
+    uint64_t* __restrict__ lists) {
   __shared__ TiledSmem sm;
+  const int L = blockIdx.x;
+  const int bx = (L / (8 * npass)) * 8 + L % 8, by = (L / 8) % npass;
+  if (bx >= nwg) return;  // the padding of the last group of eight slots
   const int t = threadIdx.x, lane = t & 63, n = lane & 31, hh = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int nwg = gridDim.x;
   const int nch = C / kTlChunk;
   // block group g (four neighbouring blocks) of workgroup x is x + g * nwg
-  const int mygroups = blockIdx.x < ngroups ? (ngroups - 1 - blockIdx.x) / nwg + 1 : 0;
+  const int mygroups = bx < ngroups ? (ngroups - 1 - bx) / nwg + 1 : 0;
   const int items = mygroups * nch;
-  const int mbase = blockIdx.y * kTlCols;
+  const int mbase = by * kTlCols;
 
   // copy lanes: 8 per 128-byte row, rows 8q + lane/8 of a 32-row quarter, q < 4
   const int lrow = lane >> 3;
@@ -342,7 +350,7 @@ __global__ __launch_bounds__(64 * kLmWaves) void lmhead_tiled_kernel(
   }
   auto issue_w = [&](const TlCursor& c, int slot) {
     // rows at or past the end read row V - 1 (their products are never used)
-    int v0 = (4 * (blockIdx.x + c.g * nwg) + w) * kLmRows;
+    int v0 = (4 * (bx + c.g * nwg) + w) * kLmRows;
     v0 = v0 < V ? v0 : V - 1;
     const int lim = V - 1 - v0;
     const uint16_t* base = wt + (int64_t)v0 * C + c.k * kTlChunk;
@@ -404,7 +412,7 @@ __global__ __launch_bounds__(64 * kLmWaves) void lmhead_tiled_kernel(
     __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     if (k == nch - 1) {
-      const int v0 = (4 * (blockIdx.x + g * nwg) + w) * kLmRows;
+      const int v0 = (4 * (bx + g * nwg) + w) * kLmRows;
 #pragma unroll
       for (int nb = 0; nb < kTlNB; ++nb) {
         const bool mvalid = mbase + nb * kLmCols + n < M;
@@ -489,7 +497,7 @@ __global__ __launch_bounds__(64 * kLmWaves) void lmhead_tiled_kernel(
       for (int nb = 0; nb < kTlNB; ++nb) {
         const int m = mbase + nb * kLmCols + n;
         if (m < M) {
-          uint64_t* out = lists + ((int64_t)m * gridDim.x + blockIdx.x) * kTopK;
+          uint64_t* out = lists + ((int64_t)m * nwg + bx) * kTopK;
 #pragma unroll
           for (int e = 0; e < kTopK; e += 2)
             *reinterpret_cast<u32x4_t*>(out + e) =
@@ -556,9 +564,10 @@ extern "C" int dflash2_lmhead_topk16(const void* hidden, int64_t hid_seq_stride,
     const int ngroups = ((V + kLmRows - 1) / kLmRows + kLmWaves - 1) / kLmWaves;
     const int per = (ngroups + kLmMaxWGs - 1) / kLmMaxWGs;
     nlists = (ngroups + per - 1) / per;
-    lmhead_tiled_kernel<<<dim3(nlists, (M + kTlCols - 1) / kTlCols), 64 * kLmWaves, 0, stream>>>(
+    const int npass = (M + kTlCols - 1) / kTlCols;
+    lmhead_tiled_kernel<<<dim3((nlists + 7) / 8 * 8 * npass), 64 * kLmWaves, 0, stream>>>(
         (const uint16_t*)hidden, hid_seq_stride, hid_row_stride, row0, N, M,
-        (const uint16_t*)weight, C, V, ngroups, lists);
+        (const uint16_t*)weight, C, V, ngroups, nlists, npass, lists);
   }
   merge16_kernel<KeyValue><<<M, kMergeThreads, (size_t)nlists * sizeof(uint64_t), stream>>>(
       nlists, lists, idx, val, KeyValue{});
