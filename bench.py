@@ -735,6 +735,7 @@ def main():
         "step_ms": rec["step_ms"],
         "ms_per_step_host_sync": rec["ms_per_step_host_sync"],
         "stage_us": rec["stage_us"],
+        "stage_cold_copies": rec["stage_cold_copies"],
         "stage_hbm": rec["stage_hbm"],
         "acceptance": rec["acceptance"],
         "mean_accepted": rec["acceptance"]["mean_accepted"],
