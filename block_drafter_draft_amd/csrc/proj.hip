@@ -131,100 +131,137 @@ __global__ __launch_bounds__(64 * kPjWaves) void proj_kernel(
   }
 }
 
-// More than 32 hidden rows: a workgroup of 4 waves owns a 64 x 64 tile (64 features x 64
-// rows) and each wave computes all 16 MFMA tiles of it over its quarter of the
-// contraction, so every operand fragment it loads feeds four products. Per step a lane
-// loads four weight pieces and four hidden pieces (columns 32 s + 8 g .. + 8 of rows
-// 16 t + r). This reads the hidden rows once per 64 features instead of once per 16:
-// about 105 MB instead of 262 MB of L2 traffic at batch 64 (512 rows, 640 features).
-constexpr int kTlWaves = 4;
-constexpr int kTlPad = 65;  // LDS row pitch (floats) of a 64 x 64 partial tile
+// Many rows, staged through LDS: a workgroup of 4 waves owns a 64 x 64 tile (64 features x
+// 64 hidden rows) and walks its share of the contraction in stages of 128 columns. Per
+// stage the workgroup copies the tile's 64 weight rows and 64 hidden rows (256 bytes of
+// each row, 32 KiB in all) into LDS with global_load_lds, each copy instruction covering
+// 4 rows x 256 contiguous bytes; two stages are in flight. Loading MFMA operands straight
+// into registers makes every load instruction touch 16 rows (the operand layout puts one
+// row in each of 16 lanes), and at batch 64 the L1 could not keep up (the address unit
+// stalled for most of the call). Each wave computes one 32 x 32 quadrant from LDS: per
+// 32-column step two weight and two hidden fragments (16-byte reads; the 16-byte chunks of
+// a row are XOR-swizzled by the row index, so the 16 rows of a read hit distinct banks)
+// and four v_mfma_f32_16x16x32_bf16. Columns past the workgroup's share are zeroed in the
+// fragments, so they add exactly nothing. At batch 64 (512 rows, 640 features, width 5120)
+// a call went from 29.5 to 25.0 us; with two 32 KiB stages in flight per workgroup and ten
+// stages each, the call is now bound by that latency chain.
+constexpr int kLsCols = 128;              // columns per stage
+constexpr int kLsChunks = kLsCols / 8;    // 16-byte chunks per row and stage
+constexpr int kLsTile = 64 * kLsChunks;   // 16-byte chunks per operand tile (16 KiB)
 
-template <int NS>
-__global__ __launch_bounds__(64 * kTlWaves) void proj_tile_kernel(
+__global__ __launch_bounds__(256) void proj_lds_kernel(
     const uint16_t* __restrict__ hid, int64_t hss, int64_t hrs, int row0, int N, int M,
     const uint16_t* __restrict__ wt, int C, int O, float* __restrict__ out, int64_t oss,
     int64_t ors, float* __restrict__ part_out) {
-  __shared__ float part[kTlWaves * 64 * kTlPad];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __shared__ u32x4_t buf[2][2][kLsTile];  // [stage slot][weight, hidden][row * 16 + chunk]
+  const int tz = blockIdx.z, ks = gridDim.z;
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform
   const int r = lane & 15, g = lane >> 4;
-  const int o0 = blockIdx.x * 64;
-  const int m0 = blockIdx.y * 64;
-  const int steps = (C + kPjStep - 1) / kPjStep;
-  const int gb = (int)((int64_t)steps * blockIdx.z / gridDim.z);
-  const int ge = (int)((int64_t)steps * (blockIdx.z + 1) / gridDim.z);
-  const int sb = gb + (int)((int64_t)(ge - gb) * w / kTlWaves);
-  const int se = gb + (int)((int64_t)(ge - gb) * (w + 1) / kTlWaves);
+  const int o0 = blockIdx.x * 64, m0 = blockIdx.y * 64;
+  const int nst = (C + kLsCols - 1) / kLsCols;
+  const int sb = (int)((int64_t)nst * tz / ks);
+  const int se = (int)((int64_t)nst * (tz + 1) / ks);
+  const int cb = sb * kLsCols, ce = se * kLsCols < C ? se * kLsCols : C;  // column share
 
-  // rows past O or M are clamped to the last one (their results are never written)
-  const uint16_t* wrow[4];
-  const uint16_t* hrow[4];
+  // copy piece i of thread t: p = t + 256 i; operand p / 1024, slot q = p % 1024 (row q / 16,
+  // physical chunk q % 16), fetching the row's logical chunk (q % 16) ^ (row % 16). Rows past
+  // O or M are clamped to the last one (their results are never written); chunks past C are
+  // clamped to the row's last whole chunk (their columns are zeroed in the fragments).
+  const uint16_t* src[8];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    wrow[u] = wt + (int64_t)min(o0 + 16 * u + r, O - 1) * C;
-    const int m = min(m0 + 16 * u + r, M - 1);
-    const int b = m / N, rr = m - b * N;
-    hrow[u] = hid + (int64_t)b * hss + (int64_t)(row0 + rr) * hrs;
+  for (int i = 0; i < 8; ++i) {
+    const int p = t + 256 * i, q = p & 1023, row = q >> 4, ch = (q & 15) ^ (row & 15);
+    if (p < 1024) {
+      src[i] = wt + (int64_t)min(o0 + row, O - 1) * C + 8 * ch;
+    } else {
+      const int m = min(m0 + row, M - 1);
+      const int b = m / N, rr = m - b * N;
+      src[i] = hid + (int64_t)b * hss + (int64_t)(row0 + rr) * hrs + 8 * ch;
+    }
   }
-  f32x4_t acc[4][4];
+  auto issue = [&](int stage, int slot) {
+    const int c0 = stage * kLsCols;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i) {
+      const int p = t + 256 * i, q = p & 1023, row = q >> 4, ch = (q & 15) ^ (row & 15);
+      int off = c0;
+      if (c0 + 8 * ch + 8 > C) off = C - 8 - 8 * ch;  // stays inside the row
+      // the wave's 64 pieces land at consecutive slots from 64 w + 256 (i % 4) of operand i / 4
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(src[i] + off),
+          (__attribute__((address_space(3))) void*)&buf[slot][i >> 2][64 * w + 256 * (i & 3)], 16,
+          0, 0);
+    }
+  };
+
+  const int wo = w & 1, wm = w >> 1;  // this wave's quadrant
+  f32x4_t acc[2][2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const u32x4_t zero = {0u, 0u, 0u, 0u};
 
-  for (int s0 = sb; s0 < se; s0 += NS) {
-    u32x4_t a[NS][4], bv[NS][4];
+  const int ns = se - sb;
+  if (ns > 0) issue(sb, 0);
+  if (ns > 1) issue(sb + 1, 1);
+  for (int s = 0; s < ns; ++s) {
+    if (s + 1 < ns)
+      __asm__ volatile("s_waitcnt vmcnt(8)" ::: "memory");  // stage s's 8 copies have landed
+    else
+      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // ... everyone's
+    const u32x4_t* A = buf[s & 1][0];
+    const u32x4_t* Bh = buf[s & 1][1];
+    const int c0 = (sb + s) * kLsCols;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int c = (s0 + s) * kPjStep + 8 * g;
-      const bool ok = (s0 + s < se) && (c < C);  // C % 8 == 0: a piece is wholly inside
+    for (int k = 0; k < kLsCols / 32; ++k) {
+      const int ch = 4 * k + g;                 // logical chunk of this lane
+      const bool live = c0 + 8 * ch < ce;       // inside the workgroup's column share
+      u32x4_t a[2], bv[2];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        a[s][u] = zero;
-        bv[s][u] = zero;
-        if (ok) {
-          a[s][u] = *reinterpret_cast<const u32x4_t*>(wrow[u] + c);
-          bv[s][u] = *reinterpret_cast<const u32x4_t*>(hrow[u] + c);
+      for (int i = 0; i < 2; ++i) {
+        const int ra = 32 * wo + 16 * i + r, rb = 32 * wm + 16 * i + r;
+        a[i] = A[ra * kLsChunks + (ch ^ (ra & 15))];
+        bv[i] = Bh[rb * kLsChunks + (ch ^ (rb & 15))];
+        if (!live) {
+          a[i] = zero;
+          bv[i] = zero;
         }
       }
-    }
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8_t, a[s][i]), __builtin_bit_cast(bf16x8_t, bv[s][j]),
-              acc[i][j], 0, 0, 0);
+              __builtin_bit_cast(bf16x8_t, a[i]), __builtin_bit_cast(bf16x8_t, bv[j]), acc[i][j],
+              0, 0, 0);
+    }
+    __syncthreads();  // every wave is done with this slot before it is refilled
+    if (s + 2 < ns) issue(sb + s + 2, s & 1);
   }
 
-  // lane (r, g) of tile (i, j) holds feature 16 i + 4 g + e of row 16 j + r; LDS [o][m]
+  // lane (r, g) of tile (i, j) holds features 16 i + 4 g .. + 3 of hidden row 16 j + r of the
+  // quadrant
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        part[(w * 64 + 16 * i + 4 * g + e) * kTlPad + 16 * j + r] = acc[i][j][e];
-  __syncthreads();
-
-  for (int e = threadIdx.x; e < 64 * 64; e += 64 * kTlWaves) {
-    const int ml = e >> 6, ol = e & 63;
-    float sum = part[ol * kTlPad + ml];
-#pragma unroll
-    for (int v = 1; v < kTlWaves; ++v) sum = __fadd_rn(sum, part[(v * 64 + ol) * kTlPad + ml]);
-    const int m = m0 + ml, o = o0 + ol;
-    if (m < M && o < O) {
+    for (int j = 0; j < 2; ++j) {
+      const int o = o0 + 32 * wo + 16 * i + 4 * g;
+      const int m = m0 + 32 * wm + 16 * j + r;
+      if (m >= M) continue;
+      float* dst;
       if (part_out) {
-        part_out[((int64_t)blockIdx.z * M + m) * O + o] = sum;
+        dst = part_out + ((int64_t)tz * M + m) * O + o;
       } else {
         const int b = m / N, rr = m - b * N;
-        out[(int64_t)b * oss + (int64_t)rr * ors + o] = sum;
+        dst = out + (int64_t)b * oss + (int64_t)rr * ors + o;
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (o + e < O) dst[e] = acc[i][j][e];
     }
-  }
 }
 
 // out[m, o] = sum over splits k in order of part[k, m, o], KS <= KMAX. Every load is issued
@@ -251,7 +288,7 @@ __global__ __launch_bounds__(256) void proj_reduce_kernel(const float* __restric
 
 struct ProjPlan {
   int mt;     // row tiles of 16 per workgroup (16-feature kernel)
-  bool tile;  // the 64 x 64 tile kernel instead
+  bool tile;  // the staged 64 x 64 tile kernel instead
   int ks;     // contraction splits over workgroups
 };
 
@@ -263,12 +300,13 @@ ProjPlan plan_proj(int M, int O, int C) {
   p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   p.tile = M >= 256 || (M > 32 && O >= 512);
   const int orows = p.tile ? 64 : kPjRows;
-  const int waves = p.tile ? kTlWaves : kPjWaves;
   const int mrows = p.tile ? 64 : 16 * p.mt;
   const int64_t tiles = (int64_t)((O + orows - 1) / orows) * ((M + mrows - 1) / mrows);
-  const int steps = (C + kPjStep - 1) / kPjStep;
   int ks = (int)((kPjTargetWGs + tiles - 1) / tiles);
-  const int by_steps = steps / waves;  // at least one step per wave
+  // at least one 32-column step per wave of the 16-feature kernel, one 128-column stage per
+  // workgroup of the tile kernel
+  const int by_steps = p.tile ? (C + kLsCols - 1) / kLsCols
+                              : (C + kPjStep - 1) / kPjStep / kPjWaves;
   ks = ks < by_steps ? ks : by_steps;
   ks = ks < kPjMaxSplit ? ks : kPjMaxSplit;
   p.ks = ks < 1 ? 1 : ks;
@@ -319,21 +357,15 @@ extern "C" int dflash2_proj(const void* hidden, int64_t hid_seq_stride, int64_t 
   const int gx = (O + orows - 1) / orows;
   const int gy = (M + mrows - 1) / mrows;
   const dim3 grid(gx, gy, p.ks);
-  // steps per wave: at most ceil(ceil(C / 32) / ks / waves)
-  const int waves = p.tile ? kTlWaves : kPjWaves;
-  const int per_wave = (((C + kPjStep - 1) / kPjStep + p.ks - 1) / p.ks + waves - 1) / waves;
+  // steps per wave of the 16-feature kernel: at most ceil(ceil(C / 32) / ks / waves)
+  const int per_wave =
+      (((C + kPjStep - 1) / kPjStep + p.ks - 1) / p.ks + kPjWaves - 1) / kPjWaves;
   const uint16_t* h = (const uint16_t*)hidden;
   const uint16_t* wt = (const uint16_t*)weight;
   const hipStream_t st = stream;
   if (p.tile) {
-    if (per_wave <= 2)
-      proj_tile_kernel<2><<<grid, 64 * kTlWaves, 0, st>>>(h, hid_seq_stride, hid_row_stride,
-                                                           row0, N, M, wt, C, O, out,
-                                                           out_seq_stride, out_row_stride, part);
-    else
-      proj_tile_kernel<4><<<grid, 64 * kTlWaves, 0, st>>>(h, hid_seq_stride, hid_row_stride,
-                                                           row0, N, M, wt, C, O, out,
-                                                           out_seq_stride, out_row_stride, part);
+    proj_lds_kernel<<<grid, 256, 0, st>>>(h, hid_seq_stride, hid_row_stride, row0, N, M, wt, C,
+                                           O, out, out_seq_stride, out_row_stride, part);
   } else if (p.mt == 1) {
     if (per_wave <= 4)
       proj_kernel<1, 4><<<grid, 64 * kPjWaves, 0, st>>>(h, hid_seq_stride, hid_row_stride, row0,
