@@ -294,7 +294,7 @@ struct ProjPlan {
 
 // The tile kernel pays off once the hidden rows are re-read enough: measured from 256 rows,
 // or from 33 rows with at least 512 features (at 112 rows x 256 features the 16-feature
-// kernel is faster).
+// kernel is faster; at 8 rows it takes 8.7 us per conv-coefficient call against 7.5).
 ProjPlan plan_proj(int M, int O, int C) {
   ProjPlan p;
   p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
