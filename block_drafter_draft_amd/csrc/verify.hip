@@ -42,6 +42,7 @@ struct ChainRec {
   int32_t pos;     // block position of the drawn token (1..N+1)
   int32_t resid;   // 1: draw from the residual of slot pos; 0: from p_t itself
   int32_t flags;   // status bits from the accept tests
+  uint64_t draw;   // word 2 of the Philox draw at position pos (the residual draw)
 };
 
 struct Ws {
@@ -112,12 +113,14 @@ __device__ void accept_chain(const float* __restrict__ tgt, int64_t row_stride, 
   if (t < 64) {
     bool acc = false, plain = false;
     int fl = 0;
+    // lane t draws for position t + 1, lane N for the bonus position N + 1 (whose word 2
+    // is the residual draw of an all-accepted chain)
+    Draw d = {};
+    if (t <= N) d = philox_draw(seed, step, (uint32_t)b, (uint32_t)(t + 1));
     if (t < N) {
-      const int j = t + 1;
       // the target gather goes out first (at a clamped, always valid index)
       const int xc = x < 0 ? 0 : (x >= V ? V - 1 : x);
       const float pt_raw = tgt[(int64_t)t * row_stride + xc];
-      Draw d = philox_draw(seed, step, (uint32_t)b, (uint32_t)j);
       const float u = uniform24(d.w[1]);
       if (x < 0 || x >= V) {
         plain = true;
@@ -137,11 +140,14 @@ __device__ void accept_chain(const float* __restrict__ tgt, int64_t row_stride, 
     const int use = (t < N && t <= first) ? fl : 0;
     const int flags = wave_or(use);
     const int plain_first = __shfl(plain ? 1 : 0, first < N ? first : 0, 64);
+    const uint32_t dlo = __shfl((uint32_t)d.w[2], first, 64);
+    const uint32_t dhi = __shfl((uint32_t)(d.w[2] >> 32), first, 64);
     if (t == 0) {
       rec->n_acc = first;
       rec->pos = first + 1;
       rec->resid = (first < N && !plain_first) ? 1 : 0;
       rec->flags = flags;
+      rec->draw = ((uint64_t)dhi << 32) | dlo;
     }
   }
   __syncthreads();
@@ -420,6 +426,8 @@ void verify_finish_kernel(
   __shared__ int sh_tok;
   __shared__ int32_t cand[kTopK];
   __shared__ float candq[kTopK];
+  __shared__ int corr_off[kTopK];      // chunk offset of a candidate's first occurrence, or -1
+  __shared__ uint64_t corr_w[kTopK];   // its residual weight
   __shared__ int32_t allc[kMaxN * kTopK];
   __shared__ float allq[kMaxN * kTopK];
   __shared__ int32_t dtok[kMaxN];
@@ -448,7 +456,7 @@ void verify_finish_kernel(
   constexpr bool kIsF32 = sizeof(typename KT::elem_t) == 4;
   constexpr int kCptMax = 4;
   const int cpt = (nchunks + kThreads - 1) / kThreads;
-  ChainRec rec_pre = {0, 1, 0, 0};
+  ChainRec rec_pre = {0, 1, 0, 0, 0};
   uint64_t zr_pre[kCptMax], zp_pre[kCptMax];
   int zf_pre[kCptMax];
   int32_t ci_pre = -1;
@@ -674,9 +682,9 @@ void verify_finish_kernel(
     __syncthreads();
     emitted = sh_tok;
   } else {
-    // every thread draws the same tau; the scan of the per-thread sums finds the chunk
-    const Draw dr = philox_draw(seed, step, (uint32_t)b, (uint32_t)rec.pos);
-    const uint64_t tau_all = scale_draw(dr.w[2], Z);
+    // every thread takes the same tau (kernel 1 made the draw); the scan of the per-thread
+    // sums finds the chunk
+    const uint64_t tau_all = scale_draw(rec.draw, Z);
     if (t == 0) sh_tok = -1;
     const uint64_t mine_z = use_resid ? my_zr : my_zp;
     const uint64_t incl_z = block_incl_scan_u64(mine_z, wsum);
@@ -705,32 +713,57 @@ void verify_finish_kernel(
     }
     __syncthreads();
     // scan the chosen chunk in index order: thread t owns EPT consecutive elements
-    const int c0 = sh_chunk * CH + t * EPT;
+    const int cbase = sh_chunk * CH;
+    const int c0 = cbase + t * EPT;
     uint64_t wgt[EPT];
     uint64_t mine = 0;
     int dummy = 0;
     float pv[EPT];
+    if (VEC && cbase + CH <= V) {
+      const float4* p4 = reinterpret_cast<const float4*>(row + c0);
+      const float4 a = p4[0], z = p4[1];
+      pv[0] = a.x; pv[1] = a.y; pv[2] = a.z; pv[3] = a.w;
+      pv[4] = z.x; pv[5] = z.y; pv[6] = z.z; pv[7] = z.w;
+    } else {
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) pv[e] = c0 + e < V ? row[c0 + e] : 0.0f;
-    float pz[EPT];
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      pz[e] = c0 + e < V ? prob_ok(pv[e], &dummy) : 0.0f;
-      wgt[e] = c0 + e < V ? quant40(pz[e]) : 0ull;
+      for (int e = 0; e < EPT; ++e) pv[e] = c0 + e < V ? row[c0 + e] : 0.0f;
     }
-    // A candidate index replaces the weight by the residual; for a repeated index the first
-    // occurrence counts, so the candidates are applied last to first. They are read from LDS
-    // one at a time (every lane reads the same word), which keeps them out of registers.
+    // A candidate index takes the residual weight instead, and for a repeated index its
+    // first occurrence counts: thread k < 16 finds whether candidate k is the first
+    // occurrence of an index inside this chunk and gathers that element with the chunk.
+    int32_t ck = -1;
+    float pk = 0.0f, qk = 0.0f;
+    bool has = false;
+    if (t < kTopK) {
+      ck = cand[t];
+      qk = candq[t];
+      has = ck >= cbase && ck < cbase + CH && ck < V;  // (cbase >= 0; unused slots hold -1)
 #pragma unroll
-    for (int k = kTopK - 1; k >= 0; --k) {
-      const int32_t ck = cand[k];
-      const float qk = candq[k];
+      for (int j = 0; j < kTopK; ++j)
+        if (j < t) has = has && cand[j] != ck;
+      if (has) pk = row[ck];
+    }
 #pragma unroll
-      for (int e = 0; e < EPT; ++e) {
-        if (ck == c0 + e && c0 + e < V) {
-          const float df = __fsub_rn(pz[e], prob_ok(qk, &dummy));
-          wgt[e] = quant40(df > 0.0f ? df : 0.0f);
-        }
+    for (int e = 0; e < EPT; ++e)
+      wgt[e] = c0 + e < V ? quant40(prob_ok(pv[e], &dummy)) : 0ull;
+    if (t < kTopK) {
+      uint64_t wk = 0;
+      if (has) {
+        const float df = __fsub_rn(prob_ok(pk, &dummy), prob_ok(qk, &dummy));
+        wk = quant40(df > 0.0f ? df : 0.0f);
+      }
+      corr_off[t] = has ? ck - cbase : -1;
+      corr_w[t] = wk;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kTopK; ++k) {
+      const int dd = corr_off[k] - t * EPT;
+      if ((unsigned)dd < (unsigned)EPT) {
+        const uint64_t wk = corr_w[k];
+#pragma unroll
+        for (int e = 0; e < EPT; ++e)
+          if (e == dd) wgt[e] = wk;
       }
     }
 #pragma unroll
