@@ -21,6 +21,14 @@ namespace {
 constexpr int kMaxN = 15;
 constexpr int kMaxR = 512;
 
+// Edge sums unrolled this many steps, so that the LDS reads of several steps are in
+// flight before their terms are added (still one at a time, in order).
+#ifndef DF2_SEL_UNROLL
+#define DF2_SEL_UNROLL 2
+#endif
+#define DF2_DO_PRAGMA(x) _Pragma(#x)
+#define DF2_UNROLL(n) DF2_DO_PRAGMA(unroll n)
+
 // LDS row stride in elements: 8 extra bf16 keep rows 16-byte aligned and shift the banks
 __host__ __device__ inline int lat_row_stride(int R) { return ((R + 7) / 8) * 8 + 8; }
 
@@ -116,6 +124,7 @@ __global__ __launch_bounds__(256) void select_lattice_kernel(
     if (kp >= npred) return;
     const float* ag = AG + kp * RS;
     // eight terms per LDS access, still added one at a time in order
+    DF2_UNROLL(DF2_SEL_UNROLL)
     for (; r < R; r += 8) {
       const u32x4_t b8 = *reinterpret_cast<const u32x4_t*>(bb + r);
       const float4 a0 = *reinterpret_cast<const float4*>(ag + r);
@@ -224,6 +233,7 @@ __global__ __launch_bounds__(256) void select_lattice_q8_kernel(
   const float* ag = AG + kp * RS;
   const float* bb = Bf + k * RS;
   float acc = 0.0f;
+  DF2_UNROLL(DF2_SEL_UNROLL)
   for (int r = 0; r < R; r += 4) {
     const float4 a4 = *reinterpret_cast<const float4*>(ag + r);
     const float4 b4 = *reinterpret_cast<const float4*>(bb + r);
@@ -244,10 +254,11 @@ __global__ __launch_bounds__(64) void select_path_kernel(
   __shared__ float S[kMaxN][kTopK][kTopK];
   __shared__ int32_t bp[kMaxN][kTopK];
   __shared__ float dp[kTopK];
-  __shared__ float e_sh[2 * kTopK];
   __shared__ float uni[kMaxN];
   __shared__ int32_t path[kMaxN];
-  __shared__ float qout[kMaxN][kTopK];
+  __shared__ float mtab[kMaxN][kTopK];         // [slot][predecessor row]: the row's maximum
+  __shared__ float ztab[kMaxN][kTopK];         // [slot][predecessor row]: its weights' sum
+  __shared__ int32_t pick_tab[kMaxN][kTopK];   // [slot][predecessor row]: the pick
   __shared__ int32_t cid[kMaxN * kTopK];
 
   // Every input load is issued first, so the prologue is one memory round trip: the
@@ -395,43 +406,62 @@ __global__ __launch_bounds__(64) void select_path_kernel(
     __syncthreads();
     for (int e = lane; e < N * kTopK; e += 64) qq[e] = (e % kTopK) == path[e / kTopK] ? 1.0f : 0.0f;
   } else {
-    // Inverse-CDF walk. Each slot's 16 weights go through LDS once; every lane then forms
-    // the running sums in k order (the same additions as the definition) and finds the
-    // pick itself, so the slot needs one barrier and no broadcast.
+    // Inverse-CDF walk. Slot i draws from the row of its predecessor, which the walk
+    // reaches only through slots 1..i-1; but every row's weights and pick can be formed
+    // before the walk, independently. Lane l takes the (slot, predecessor row) pairs l,
+    // l + 64, ...: the row's maximum, its 16 weights exp_c((s - max) / T), their running
+    // sums in k order, and the pick (the first k whose running sum exceeds u_i Z). The
+    // walk then only follows the picks, and q = weight / Z is formed for the rows it took
+    // (their weights formed again, the same way). Slot 1 has only row 0 (the anchor).
     if (lane < N) uni[lane] = uniform24(philox_draw(seed, step, (uint32_t)b, (uint32_t)(lane + 1)).w[0]);
     __syncthreads();
-    int prev = 0;
-    for (int i = 1; i <= N; ++i) {
-      const int row = i == 1 ? 0 : prev;
-      float s = lane < kTopK ? S[i - 1][row][lane] : -3.40282347e38f;
-      // the maximum is exact in any order: within lanes 0..15, then lane 0's to all
-      const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(row16_max(s)), 0));
-      const float e = exp_c(__fmul_rn(__fsub_rn(s, m), invT));
-      if (lane < kTopK) e_sh[(i & 1) * kTopK + lane] = e;  // two buffers: no barrier before the write
-      __syncthreads();
-      float ev[kTopK];
+    for (int pr = lane; pr < N * kTopK; pr += 64) {
+      const int i = pr / kTopK + 1, row = pr % kTopK;
+      if (i > 1 || row == 0) {
+        float sv[kTopK];
 #pragma unroll
-      for (int kk = 0; kk < kTopK; ++kk) ev[kk] = e_sh[(i & 1) * kTopK + kk];
-      const float u = uni[i - 1];
-      float Z = 0.0f;
-      int pick = -1;
-      float C[kTopK];
+        for (int k4 = 0; k4 < kTopK; k4 += 4) {
+          const float4 v4 = *reinterpret_cast<const float4*>(&S[i - 1][row][k4]);
+          sv[k4] = v4.x;
+          sv[k4 + 1] = v4.y;
+          sv[k4 + 2] = v4.z;
+          sv[k4 + 3] = v4.w;
+        }
+        float m = sv[0];
 #pragma unroll
-      for (int kk = 0; kk < kTopK; ++kk) {
-        Z = __fadd_rn(Z, ev[kk]);
-        C[kk] = Z;
+        for (int k = 1; k < kTopK; ++k) m = sv[k] > m ? sv[k] : m;  // exact in any order
+        float C[kTopK];
+        float Z = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kTopK; ++k) {
+          const float e = exp_c(__fmul_rn(__fsub_rn(sv[k], m), invT));
+          Z = __fadd_rn(Z, e);
+          C[k] = Z;
+        }
+        const float tau = __fmul_rn(uni[i - 1], Z);
+        int pick = -1;
+#pragma unroll
+        for (int k = kTopK - 1; k >= 0; --k)
+          if (C[k] > tau) pick = k;
+        pick_tab[i - 1][row] = pick < 0 ? kTopK - 1 : pick;
+        mtab[i - 1][row] = m;
+        ztab[i - 1][row] = Z;
       }
-      const float tau = __fmul_rn(u, Z);
-#pragma unroll
-      for (int kk = kTopK - 1; kk >= 0; --kk)
-        if (C[kk] > tau) pick = kk;
-      pick = pick < 0 ? kTopK - 1 : pick;
-      if (lane < kTopK) qout[i - 1][lane] = __fdiv_rn(e, Z);
-      if (lane == 0) path[i - 1] = pick;
-      prev = pick;
     }
     __syncthreads();
-    for (int e = lane; e < N * kTopK; e += 64) qq[e] = qout[e / kTopK][e % kTopK];
+    if (lane == 0) {
+      int prev = 0;
+      for (int i = 1; i <= N; ++i) {
+        prev = pick_tab[i - 1][i == 1 ? 0 : prev];
+        path[i - 1] = prev;
+      }
+    }
+    __syncthreads();
+    for (int e = lane; e < N * kTopK; e += 64) {
+      const int i = e / kTopK + 1, row = i == 1 ? 0 : path[i - 2];
+      const float w = exp_c(__fmul_rn(__fsub_rn(S[i - 1][row][e % kTopK], mtab[i - 1][row]), invT));
+      qq[e] = __fdiv_rn(w, ztab[i - 1][row]);
+    }
   }
   if (lane < N) {
     sl[lane] = path[lane];
