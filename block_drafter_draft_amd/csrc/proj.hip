@@ -162,7 +162,7 @@ __global__ __launch_bounds__(256) void proj_lds_kernel(
   const int nst = (C + kLsCols - 1) / kLsCols;
   const int sb = (int)((int64_t)nst * tz / ks);
   const int se = (int)((int64_t)nst * (tz + 1) / ks);
-  const int cb = sb * kLsCols, ce = se * kLsCols < C ? se * kLsCols : C;  // column share
+  const int ce = se * kLsCols < C ? se * kLsCols : C;  // end of the column share
 
   // copy piece i of thread t: p = t + 256 i; operand p / 1024, slot q = p % 1024 (row q / 16,
   // physical chunk q % 16), fetching the row's logical chunk (q % 16) ^ (row % 16). Rows past

@@ -281,7 +281,6 @@ __global__ __launch_bounds__(kThreads) void topk_wave_kernel(
     if (__ballot(kmax >= Tf) == 0) return true;
     cnt = __builtin_amdgcn_readfirstlane(cnt);  // wave-uniform: lets the count live in an SGPR
     const int cnt0_fast = cnt;
-    const uint64_t below = (1ull << lane) - 1;
     // each element position's ballot comes from one 16-bit compare of its half word
     const uint16_t tf16 = (uint16_t)Tf;
 #pragma unroll
