@@ -81,7 +81,8 @@ def _rand(rng, shape, scale):
 def test_lmhead_small_shapes(d2, B, N, C, V):
     # up to 32 hidden rows: ragged last vocabulary block, a single block, V = 16; more
     # than 32 (the tiled kernel, 128 rows per pass): a ragged row tile, two and four passes,
-    # a vocabulary smaller than one workgroup's four blocks
+    # a vocabulary smaller than one workgroup's eight blocks, and last block groups that
+    # are only partly inside the vocabulary
     rng = np.random.default_rng(B * 1000 + N * 100 + C + V)
     hid = _rand(rng, (B, N + 1, C), 2.0)
     w = _rand(rng, (V, C), 1.0 / np.sqrt(C))
