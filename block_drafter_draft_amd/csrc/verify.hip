@@ -11,6 +11,8 @@
 //             every workgroup of the sequence recomputes it and then reads only the row it
 //             will draw from: the chunk sums of the integer weights floor(w * 2^40), both
 //             for p_t itself and with the 16 candidates' residual max(0, p_t - q) swapped in.
+//             The chain record (accepted count, draw position, residual or not, status
+//             bits, and word 2 of the Philox draw at that position) goes to the workspace.
 // Kernel 2 (grid: G workgroups per sequence):
 //   greedy  - every workgroup reduces row 0's chunk maxima and checks proposal 1. Rejected:
 //             workgroup 0 writes the result. Accepted: the G workgroups stream rows 1..N over
@@ -20,8 +22,9 @@
 //             through agent-scope atomics, which are coherent across the XCDs' L2 caches
 //             without a release fence (a fence would write back the whole L2).
 //   sampled - workgroup 0 picks the chunk holding the draw from the chunk sums and scans
-//             that one chunk in index order. Integer weights make the draw independent of
-//             the summation order, so it is bit-exact.
+//             that one chunk in index order (each candidate's residual weight computed once,
+//             by its own thread). Integer weights make the draw independent of the
+//             summation order, so it is bit-exact.
 #include <algorithm>
 
 #include "common.hpp"
