@@ -210,10 +210,12 @@ def test_conv_shapes(d2, P, C):
     run_conv(d2, wl.to_bf16_bits(x), base, delta, f"bf16 P{P} C{C}", BF16_TOL)
 
 
-@pytest.mark.parametrize("B,P,C", [(40, 16, 4096), (128, 3, 1024), (26, 8, 5120), (33, 1, 4000)])
+@pytest.mark.parametrize("B,P,C", [(40, 16, 4096), (128, 3, 1024), (26, 8, 5120), (33, 1, 4000),
+                                   (300, 1, 528)])
 def test_conv_large_batches(d2, B, P, C):
     # large batches (P up to 16, f32 and bf16, a ragged channel count): the same bounds,
-    # and identity taps reproduce the input exactly
+    # and identity taps reproduce the input exactly. From 256 rows a thread takes two
+    # positions: odd P and P = 1 leave the last pair half empty.
     rng = np.random.default_rng(90 + B + P)
     x = rng.standard_normal((B, P, C)).astype(np.float32)
     base = rng.uniform(-1, 1, (2, C)).astype(np.float32)
